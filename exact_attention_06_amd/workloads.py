@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module only draws inputs; it holds none of the attention arithmetic, and
+both the GPU path and the CPU oracle read the tensors it returns.
+
+Recipe (the pages draw their examples with ``torch.randn``; the workloads
+below have the shapes, sizes and value distributions of the benchmark cases):
+- ``g = torch.Generator('cpu').manual_seed(seed)``; Q, then K, then V are drawn
+  with ``torch.randn(B, H, N, d, dtype=float32, generator=g)`` (iid N(0, 1)),
+  then cast to bfloat16 (round to nearest even) where the workload is bf16.
+- FP8 workload: after Q, K, V, for each of Q, K, V in that order exactly
+  floor(0.001 * numel) positions are chosen without replacement
+  (``torch.randperm(numel, generator=g)``) and multiplied by 20 (outliers);
+  then the random +-1 sign vector of the Hadamard rotation is drawn as
+  ``where(torch.rand(d, generator=g) > 0.5, 1, -1)``. The signs are the only
+  random numbers the method itself uses, so they are an input here.
+- The softmax scale is 1/sqrt(d) throughout.
+
+Layout is [B, H, N, d], contiguous.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f32", "bf16" or "fp8"
+    causal: tuple       # causal settings this workload is run with
+    seed: int
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, causal: bool) -> float:
+        """Counted FLOPs: 4 B H N^2 d, halved for causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if causal else f
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32", 1, 2, 256, 64, "f32", (False,), 1,
+                 "tiny reference case, fp32 in and out"),
+        Workload("b4h16n2k_d128", 4, 16, 2048, 128, "bf16", (False, True), 2,
+                 "bf16, non-causal and causal"),
+        Workload("long_n16k_d128", 1, 32, 16384, 128, "bf16", (True,), 3,
+                 "long context, causal"),
+        Workload("b8h16n4k_d64", 8, 16, 4096, 64, "bf16", (False,), 4, "head-dim sweep, d=64"),
+        Workload("b8h16n4k_d256", 8, 16, 4096, 256, "bf16", (False,), 5, "head-dim sweep, d=256"),
+        Workload("fp8_b4h16n8k_d128", 4, 16, 8192, 128, "fp8", (False,), 6,
+                 "e4m3 with outliers, random-Hadamard rotation, per-64-row scales"),
+        Workload("b4h16n8k_d128", 4, 16, 8192, 128, "bf16", (False, True), 7,
+                 "headline bf16 N=8k d=128 (same shape as the fp8 case)"),
+    ]
+}
+
+OUTLIER_FRACTION = 0.001
+OUTLIER_FACTOR = 20.0
+
+
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16"):
+    """Draw Q, K, V iid N(0, 1) on the CPU; returns three contiguous tensors of ``dtype``."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    k = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    v = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    if dtype == "bf16":
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    elif dtype not in ("f32", "fp8"):
+        raise ValueError(f"unknown dtype {dtype}")
+    return q, k, v
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int):
+    """FP8 workload inputs: float32 Q, K, V with outliers, and the +-1 rotation signs [d]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    k = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    v = torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    n_out = int(math.floor(OUTLIER_FRACTION * q.numel()))
+    for t in (q, k, v):
+        idx = torch.randperm(t.numel(), generator=g)[:n_out]
+        flat = t.view(-1)
+        flat[idx] = flat[idx] * OUTLIER_FACTOR
+    signs = torch.where(torch.rand(d, generator=g) > 0.5, 1.0, -1.0).to(torch.float32)
+    return q, k, v, signs
+
+
+def make_inputs(w: Workload):
+    """Inputs for a named workload: (q, k, v) or, for fp8, (q32, k32, v32, signs)."""
+    if w.dtype == "fp8":
+        return make_fp8_inputs(w.B, w.H, w.N, w.d, w.seed)
+    return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype)
