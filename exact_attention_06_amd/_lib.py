@@ -1,0 +1,161 @@
+"""ctypes binding of ``libfa.so`` (the C ABI in include/fa.h).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels behind the C entry points. PyTorch supplies device memory and the
+stream; there is no CPU or PyTorch fallback, and a missing library or a
+non-GPU tensor is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libfa.so")
+
+FA_OK = 0
+FA_F32 = 0
+FA_BF16 = 1
+STATUS_NAMES = {
+    0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_ALIGN", -3: "FA_ERR_SHAPE", -4: "FA_ERR_HEADDIM",
+    -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
+}
+EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero status returned by the attention library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_06_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_prep_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    L.fa_prep_fp8.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.fa_fwd_fp8.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        raise FAError(status, status_string(status))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("attention tensors must be contiguous GPU tensors")
+
+
+def _bhnd(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, want_lse=True, stream=None):
+    """O = softmax(scale Q K^T [causal]) V and the row logsumexp, on the GPU.
+
+    q, k, v: contiguous [B, H, N, d] torch tensors on the GPU, all float32 or all
+    bfloat16. ``o`` / ``lse`` may be given (preallocated outputs) or are
+    allocated here. Returns (o, lse); lse is None if ``want_lse`` is False and
+    none was given.
+    """
+    B, H, N, d = _bhnd(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same [B, H, N, d] shape")
+    if q.dtype == torch.bfloat16:
+        dt = FA_BF16
+    elif q.dtype == torch.float32:
+        dt = FA_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _require_gpu(q, k, v, o, lse)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale, int(bool(causal)), dt,
+                        _stream(stream)))
+    return o, lse
+
+
+def fa_prep_fp8(x, signs=None, x8=None, s=None, *, stream=None):
+    """Rotate (if ``signs`` is given) and block-quantise float32 x [B, H, N, d] to e4m3.
+
+    Returns (x8 uint8 [B, H, N, d], s float32 [B, H, ceil(N/64)]).
+    """
+    B, H, N, d = _bhnd(x)
+    if x.dtype != torch.float32:
+        raise ValueError("fa_prep_fp8 takes float32 input")
+    nsb = (N + 63) // 64
+    if x8 is None:
+        x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((B, H, nsb), dtype=torch.float32, device=x.device)
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d):
+        raise ValueError("signs must be float32 with d entries")
+    _require_gpu(x, x8, s, signs)
+    _check(lib().fa_prep_fp8(_ptr(x), _ptr(x8), _ptr(s), _ptr(signs), B, H, N, d, _stream(stream)))
+    return x8, s
+
+
+def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=False, want_lse=True, stream=None):
+    """Attention forward on e4m3 codes with per-64-row scales; returns (o bfloat16, lse)."""
+    B, H, N, d = _bhnd(q8)
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or t.shape != q8.shape:
+            raise ValueError("q8, k8, v8 must be uint8 [B, H, N, d] code tensors")
+    nsb = (N + 63) // 64
+    for t in (sq, sk, sv):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, nsb):
+            raise ValueError("scales must be float32 [B, H, ceil(N/64)]")
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _require_gpu(q8, k8, v8, sq, sk, sv, o, lse)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv), _ptr(o), _ptr(lse),
+                            B, H, N, d, scale, int(bool(causal)), _stream(stream)))
+    return o, lse

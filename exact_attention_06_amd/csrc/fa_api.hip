@@ -1,0 +1,90 @@
+// C ABI of the attention library (declared in include/fa.h): argument checks on the host,
+// then dispatch to the gfx950 kernels. No allocation, no synchronisation, no fallback: an
+// unsupported argument is an error code, never a silent slower path.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool headdim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+// common shape/scale checks; returns FA_OK or the first error
+int check_common(int B, int H, int N, int d, float scale, int causal) {
+    if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+    if (!headdim_ok(d)) return FA_ERR_HEADDIM;
+    if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    // element offsets are computed in 64-bit; the grid and per-head row counts must fit int32
+    const long long rows = (long long)B * H * (long long)N;
+    if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, float scale,
+           int causal, int dtype, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == FA_BF16) return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s));
+    return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s));
+}
+
+int fa_prep_fp8(const float* x, void* x8, float* sc, const float* signs, int B, int H, int N, int d, void* stream) {
+    int st = check_common(B, H, N, d, 1.f, 0);
+    if (st != FA_OK) return st;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if (!x || !x8 || !sc) return FA_ERR_NULLPTR;
+    if (!aligned16(x) || !aligned16(x8) || !aligned16(sc) || (signs && !aligned16(signs))) return FA_ERR_ALIGN;
+    return from_hip(fa::launch_prep_fp8(x, x8, sc, signs, B * H, N, d, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk, const float* sv,
+               void* o, float* lse, int B, int H, int N, int d, float scale, int causal, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if (!q8 || !k8 || !v8 || !sq || !sk || !sv || !o) return FA_ERR_NULLPTR;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(sq) | reinterpret_cast<uintptr_t>(sk) | reinterpret_cast<uintptr_t>(sv)) & 3u)
+        return FA_ERR_ALIGN;
+    return from_hip(fa::launch_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, B * H, N, d, scale, causal != 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULLPTR: return "a required pointer is NULL";
+        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case FA_ERR_SHAPE: return "invalid shape (negative size or too many rows)";
+        case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64, 128 or 256)";
+        case FA_ERR_DTYPE: return "unsupported dtype";
+        case FA_ERR_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+/*
+ * fa.h - C ABI of the exact-attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. For every batch b and head h, with Q, K, V the [N, d]
+ * slices of that (b, h):
+ *
+ *     S = scale * Q K^T              (N x N, never written to memory)
+ *     S[i][j] = -inf  for j > i      (only when causal != 0)
+ *     O = softmax_rows(S) V          (N x d)
+ *     LSE[i] = log(sum_j exp(S[i][j]))   (natural log, one fp32 per query row)
+ *
+ * This is exact attention as defined on the page "Learn: The Memory Wall &
+ * FlashAttention", section 4 "The attention memory problem", computed in one
+ * fused kernel with the online-softmax recurrence of section 5.1 of the same
+ * page (running max, running sum, rescaled unnormalised accumulator, one
+ * division at the end) and the FA2 work split of "FlashAttention 2 & 3: Work
+ * Partitioning, Warp Specialization & FP8" (sections "Edit 1" to "Edit 3").
+ * LSE is the per-row logsumexp L = m + log l that the same page's section "The
+ * backward pass" says the forward saves. The causal mask is top-left aligned:
+ * query i sees keys 0..i (the mask of that page's reference loop).
+ *
+ * Conventions for every entry point:
+ * - Tensors are dense, contiguous, row-major [B, H, N, d] ("BHND": batch, head,
+ *   sequence, head dim); LSE is [B, H, N] fp32. Queries and keys have the same
+ *   length N.
+ * - Pointers are device pointers (HIP device memory) owned by the caller. The
+ *   library never allocates, frees or copies host memory, and never
+ *   synchronises: work is enqueued on `stream` (a hipStream_t passed as void*,
+ *   NULL for the null stream) and the call returns once it is enqueued.
+ * - Arguments are checked on the host before anything is launched; on an
+ *   argument error nothing is launched and no output is written. No exception
+ *   crosses the ABI. After a launch, a launch error is reported as
+ *   FA_ERR_LAUNCH (the state of the outputs is then undefined).
+ * - B, H or N equal to 0 is an empty problem: FA_OK, nothing is launched.
+ *   N need not be a multiple of any tile size.
+ * - NaN or infinite inputs are not trapped; they propagate into the outputs.
+ * - All entry points are safe to call from several host threads on different
+ *   streams; calls on one stream execute in order.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULLPTR = -1,   /* a required pointer is NULL */
+    FA_ERR_ALIGN = -2,     /* a pointer is not 16-byte aligned */
+    FA_ERR_SHAPE = -3,     /* B, H or N negative, or B*H*N*d does not fit the index range */
+    FA_ERR_HEADDIM = -4,   /* d is not 64, 128 or 256 */
+    FA_ERR_DTYPE = -5,     /* dtype is not one of fa_dtype */
+    FA_ERR_SCALE = -6,     /* scale is not finite and > 0 */
+    FA_ERR_LAUNCH = -7,    /* the HIP runtime reported an error at launch */
+    FA_ERR_ARG = -8        /* any other invalid argument (e.g. causal not 0/1) */
+} fa_status;
+
+typedef enum {
+    FA_F32 = 0,   /* float32 Q, K, V and O; fp32 arithmetic throughout */
+    FA_BF16 = 1   /* bfloat16 Q, K, V and O; bf16 MFMA products, fp32 accumulation and softmax */
+} fa_dtype;
+
+/*
+ * fa_fwd - fused attention forward.
+ *   q, k, v  [B, H, N, d] of `dtype` (input, not modified).
+ *   o        [B, H, N, d] of `dtype` (output). Must not overlap the inputs.
+ *   lse      [B, H, N] fp32 (output), natural-log logsumexp of each row of the
+ *            scaled, masked scores; may be NULL to skip it.
+ *   d        64, 128 or 256.  scale: finite, > 0 (usually 1/sqrt(d)).
+ *   causal   0 or 1.   dtype: an fa_dtype value.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_prep_fp8 - incoherent rotation and per-block E4M3 quantisation of one tensor.
+ *
+ * Sources: "FlashAttention 2 & 3" page, section "Incoherent processing: rotate
+ * away the outliers" (x -> x M with M = (1/sqrt(d)) H D, H the Sylvester
+ * Hadamard matrix, D a diagonal of +-1 signs) and the fake quantiser there
+ * (scale = amax / 448, 1 when amax is 0); "FlashAttention-3: How Warp
+ * Specialization ..." page, section 4 "Technique 3" (block-wise scales, e4m3
+ * with magnitudes up to 448).
+ *
+ *   x      [B, H, N, d] fp32 (input).
+ *   x8     [B, H, N, d] bytes (output): OCP E4M3 codes (bias 7, max 448, no
+ *          infinities), rounded to nearest even, saturated at +-448.
+ *   s      [B, H, ceil(N/64)] fp32 (output): one scale per block of 64 rows
+ *          (sequence positions) of one (b, h) across all d columns; the last
+ *          block of a ragged N covers the remaining rows. s = amax / 448 of the
+ *          rotated block (1 when the block is all zero) and
+ *          x8 = e4m3(x_rotated / s), the division done in fp32.
+ *   signs  [d] fp32 of +1/-1 (input), the diagonal D; NULL skips the rotation
+ *          (plain block quantisation, e.g. for V).
+ * The rotation is computed in fp32 with a fast Walsh-Hadamard transform.
+ */
+int fa_prep_fp8(const float* x, void* x8, float* s, const float* signs,
+                int B, int H, int N, int d, void* stream);
+
+/*
+ * fa_fwd_fp8 - fused attention forward on E4M3 inputs with per-block scales.
+ *
+ * Source: "FlashAttention-3: How Warp Specialization ..." page, section 4:
+ * the score tile is s_Q * s_K * (Q8 K8^T) with FP32 accumulation, the softmax
+ * statistics and the output accumulator stay in high precision, and P is
+ * converted to FP8 for the second product ("FlashAttention 2 & 3" page,
+ * section "What stays in higher precision").
+ *
+ *   q8, k8, v8  [B, H, N, d] E4M3 codes (as written by fa_prep_fp8; Q and K
+ *               rotated with the same signs, V usually not rotated).
+ *   sq, sk, sv  [B, H, ceil(N/64)] fp32 block scales of q8, k8, v8.
+ *   o           [B, H, N, d] bfloat16 (output) = the attention of the
+ *               dequantised inputs (if V was rotated, O is in the rotated basis).
+ *   lse         [B, H, N] fp32 (output) or NULL, as in fa_fwd.
+ *   d           64, 128 or 256.  scale, causal: as in fa_fwd.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+               const float* sq, const float* sk, const float* sv,
+               void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream);
+
+/* fa_status_string - static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* fa_version - library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

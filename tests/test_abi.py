@@ -1,0 +1,101 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h declares, and
+rejects bad arguments on the host before anything is launched (no compute call here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from exact_attention_06_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_attention_06_amd.build import build
+
+        build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(L):
+    from exact_attention_06_amd import _lib
+
+    assert L.fa_version() == 100
+    for code, name in _lib.STATUS_NAMES.items():
+        s = _lib.status_string(code)
+        assert s and s != "unknown status", name
+    assert _lib.status_string(12345) == "unknown status"
+
+
+P = 0x10000   # a 16-byte aligned fake device address: never dereferenced, validation fails first
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=128, scale=0.088, causal=0, dtype=1):
+    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_fwd_argument_errors(L):
+    assert fwd(L, d=96) == -4
+    assert fwd(L, d=32) == -4
+    assert fwd(L, scale=0.0) == -6
+    assert fwd(L, scale=-1.0) == -6
+    assert fwd(L, scale=float("inf")) == -6
+    assert fwd(L, scale=float("nan")) == -6
+    assert fwd(L, causal=2) == -8
+    assert fwd(L, dtype=2) == -5
+    assert fwd(L, B=-1) == -3
+    assert fwd(L, N=-5) == -3
+    assert fwd(L, B=1 << 16, H=1 << 16, N=1) == -3     # B*H*N beyond the int32 row range
+    assert fwd(L, q=None) == -1
+    assert fwd(L, o=None) == -1
+    assert fwd(L, k=P + 8) == -2
+    assert fwd(L, lse=P + 4) == -2
+
+
+def test_empty_problem_is_ok_without_launch(L):
+    # nothing to do: no pointer is touched and no kernel is launched
+    assert fwd(L, q=None, k=None, v=None, o=None, lse=None, N=0) == 0
+    assert fwd(L, q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+    assert L.fa_prep_fp8(None, None, None, None, 0, 4, 64, 128, None) == 0
+    assert L.fa_fwd_fp8(None, None, None, None, None, None, None, None, 2, 0, 64, 128, 0.1, 0, None) == 0
+
+
+def test_fp8_argument_errors(L):
+    assert L.fa_prep_fp8(P, P, P, None, 1, 1, 64, 100, None) == -4
+    assert L.fa_prep_fp8(None, P, P, None, 1, 1, 64, 128, None) == -1
+    assert L.fa_prep_fp8(P + 4, P, P, None, 1, 1, 64, 128, None) == -2
+    assert L.fa_fwd_fp8(P, P, P, P, P, P, P, P, 1, 1, 64, 128, 0.0, 0, None) == -6
+    assert L.fa_fwd_fp8(P, P, P, None, P, P, P, P, 1, 1, 64, 128, 0.1, 0, None) == -1
+    assert L.fa_fwd_fp8(P, P, P, P + 2, P, P, P, P, 1, 1, 64, 128, 0.1, 0, None) == -2
+    assert L.fa_fwd_fp8(P, P, P, P, P, P, P, P, 1, 1, 64, 128, 0.1, 3, None) == -8
+
+
+def test_python_binding_rejects_cpu_tensors(L):
+    import torch
+
+    from exact_attention_06_amd import fa_fwd
+
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa_fwd(q, q, q, o=torch.empty_like(q), lse=torch.empty(1, 1, 64))
