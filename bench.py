@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--only-headline] [--no-cpu]
+
+Prints ONE JSON line. A step is one fused forward (fa_fwd) over the headline
+workload: B=4, H=16, N=8192, d=128, bfloat16 Q/K/V/O, non-causal, inputs
+resident in HBM. Throughput counts 4*B*H*N^2*d FLOPs per step (halved for
+causal), the same count for every backend. Also reported:
+
+- ``roofline``: the forward kernel against the dense bf16 MFMA peak (2.5
+  PFLOP/s published for MI355X), with its average launch time measured by HIP
+  events on the stream the kernel is launched on; ``traffic`` (HBM bytes per
+  launch, from rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by the same counters
+  on a plain copy of known size) is read from profiles/ and is null if the
+  kernel sources changed since those counters were taken;
+- ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
+  same workload on the host cores (a reported baseline, not the target);
+- ``extra``: the causal headline, the other workloads (including the FP8 path:
+  rotation/quantisation of Q, K, V plus the FP8 forward) and the FP8
+  quantiser's HBM throughput.
+
+``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
+rocprofv3 byte counters); ``--only-headline`` skips the extra workloads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
+HEADLINE = "b4h16n8k_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd_bf16_b4h16n8k_d128.txt")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only-headline", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calib-copy", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counter readings are still current."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """Stored HBM bytes per launch of the headline kernel, or None if missing or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def progress(msg: str) -> None:
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def time_launches(torch, fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per call of fn (which launches on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def calib_copy(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = time_launches(torch, lambda: dst.copy_(src), 10, 2)
+    print(json.dumps({"calib_copy_bytes": n, "ms": ms, "GB/s": 2 * n / ms / 1e6}))
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """Time the float64 oracle on whole heads of the workload until ~budget_s of CPU work."""
+    import numpy as np
+
+    from exact_attention_06_amd.workloads import make_qkv
+    from oracle.attention import attention_head_fp64
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.seed, "bf16")   # the same inputs as the GPU run
+    heads, secs = 0, 0.0
+    while secs < budget_s and heads < w.B * w.H:
+        b, hi = divmod(heads, w.H)
+        qh, kh, vh = (x[b, hi].float().numpy().astype(np.float64) for x in (q, k, v))
+        t0 = time.perf_counter()
+        attention_head_fp64(qh, kh, vh, w.scale, False)
+        secs += time.perf_counter() - t0
+        heads += 1
+    flops = heads * 4.0 * w.N * w.N * w.d
+    return {
+        "value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"first {heads} of {w.B * w.H} heads of the workload (all {w.N} query rows each, "
+                  f"non-causal), float64 three-pass oracle, {secs:.1f} s; value = 4*N^2*d per head / time",
+        "seconds": round(secs, 2), "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention forward "
+              "is not sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.calib_copy:
+        calib_copy(torch)
+        return 0
+
+    from exact_attention_06_amd import fa_fwd, fa_fwd_fp8, fa_prep_fp8
+    from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_inputs, make_qkv
+
+    def bf16_case(w, causal, steps, warmup):
+        q, k, v = (x.cuda() for x in make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        ms = time_launches(torch, lambda: fa_fwd(q, k, v, o, lse, causal=causal), steps, warmup)
+        del q, k, v, o, lse
+        return ms
+
+    # ---------------- headline
+    w = WORKLOADS[HEADLINE]
+    flops = w.flops(False)
+    ms = bf16_case(w, False, args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    progress(f"headline {ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    traffic = read_traffic()
+    result = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d) and % of MFMA peak, bf16 N=8k d=128",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1))",
+        "config": {"workload": f"fa_fwd B={w.B} H={w.H} N={w.N} d={w.d} bf16 non-causal",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    extra = {}
+    if not args.only_headline:
+        s2, w2 = max(5, args.steps // 2), 2
+        ms_c = bf16_case(w, True, args.steps, args.warmup)
+        extra["headline_causal"] = {"ms": round(ms_c, 4), "TFLOP/s": round(w.flops(True) / ms_c / 1e9, 1)}
+        for name, causal in [("b4h16n2k_d128", False), ("b4h16n2k_d128", True), ("long_n16k_d128", True),
+                             ("b8h16n4k_d64", False), ("b8h16n4k_d256", False)]:
+            wx = WORKLOADS[name]
+            m = bf16_case(wx, causal, s2, w2)
+            extra[f"{name}{'_causal' if causal else ''}"] = {
+                "ms": round(m, 4), "TFLOP/s": round(wx.flops(causal) / m / 1e9, 1)}
+            progress(f"{name} causal={causal}: {m:.3f} ms")
+        # FP8 path: prep of Q, K (rotated) and V, then the FP8 forward
+        wf = WORKLOADS["fp8_b4h16n8k_d128"]
+        q, k, v, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))
+        q8, sq = fa_prep_fp8(q, signs)
+        k8, sk = fa_prep_fp8(k, signs)
+        v8, sv = fa_prep_fp8(v)
+        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device="cuda")
+        m_fwd = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), s2, w2)
+        m_prep = time_launches(torch, lambda: fa_prep_fp8(q, signs, q8, sq), s2, w2)
+        prep_bytes = q.numel() * 5 + sq.numel() * 4
+        extra["fp8_b4h16n8k_d128"] = {
+            "fwd_ms": round(m_fwd, 4), "fwd_TFLOP/s": round(wf.flops(False) / m_fwd / 1e9, 1),
+            "prep_ms_per_tensor": round(m_prep, 4),
+            "prep_GB/s": round(prep_bytes / m_prep / 1e6, 1),
+            "path_ms": round(m_fwd + 3 * m_prep, 4),
+            "path_TFLOP/s": round(wf.flops(False) / (m_fwd + 3 * m_prep) / 1e9, 1),
+        }
+        del q, k, v, q8, k8, v8, o, lse
+        progress(f"fp8: fwd {m_fwd:.3f} ms, prep {m_prep:.3f} ms per tensor")
+        result["extra"] = extra
+    # calibration GEMM (hipBLASLt via torch): what a plain bf16 GEMM sustains on this GPU now
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty_like(a)
+    g_ms = time_launches(torch, lambda: torch.mm(a, b, out=c), 10, 3)
+    gemm_tflops = 2.0 * 8192 ** 3 / g_ms / 1e9
+    result["calibration_gemm"] = {"shape": "8192x8192x8192 bf16 torch.mm", "TFLOP/s": round(gemm_tflops, 1),
+                                  "attention_frac_of_gemm": round(tflops / gemm_tflops, 4)}
+    del a, b, c
+    progress(f"calibration gemm {gemm_tflops:.1f} TFLOP/s")
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w)
+        progress("cpu baseline done")
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
