@@ -67,6 +67,20 @@ __device__ __forceinline__ int swap_bits23(int r) { return (r & ~12) | ((r & 4) 
 // 4-lane-group-of-the-result row index of register i for lane half h (D layout above)
 __device__ __forceinline__ constexpr int mfma32_row(int i, int h) { return 8 * (i / 4) + 4 * h + (i % 4); }
 
+// Buffer loads over a resource whose range check turns reads past the end into zeros.
+// The builtins are wrapped in plain device functions: called directly from the kernel
+// template with per-thread offsets they make the host compilation pass drop the kernel's
+// launch stub (a silent substitution failure in clang), which leaves the library with an
+// undefined symbol.
+// lds_dma16: 16 bytes per lane from r + voff straight into LDS at lds + 16 * lane
+// (lds must be the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
 // XCD-aware work index: the dispatcher hands consecutive workgroup ids to the 8 XCDs in
 // turn; remap so that each XCD walks a contiguous range of work items (a contiguous range
 // of heads shares that XCD's L2).

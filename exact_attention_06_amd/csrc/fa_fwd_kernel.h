@@ -17,15 +17,21 @@
 //   already the B operand (P^T) of O^T += V_j^T P^T in bf16; P never leaves registers.
 // - V^T is read from the row-major bf16 V tile with ds_read_b64_tr_b16 (8 keys of one d
 //   column per lane in two reads).
-// - K/V tiles are double-buffered in LDS: the global loads of block j+1 are issued before
-//   the math on block j and written to the other buffer after it; one barrier per block.
+// - K/V blocks go from HBM straight into LDS (buffer_load ... lds, no staging registers);
+//   rows past N read as zero through the buffer's range check. Tiles are unpadded and
+//   XOR-swizzled in 16-byte chunks so that the MFMA operand reads and the transposing V
+//   reads are free of bank conflicts.
+// - Two-stage software pipeline: while the softmax of block j runs on the vector ALUs, the
+//   scores of block j+1 are computed on the matrix cores (the same idea as the
+//   intra-warpgroup overlap on the FA2/FA3 pages), then O += P_j V_j. K is double-buffered
+//   one block ahead of V; one barrier per block.
 // - The accumulator is rescaled only when a row maximum grows by more than 2^TAU (the
 //   conditional rescaling of the FA4 section of the memory-wall page). The result stays
 //   exact (numerator and denominator use the same reference); P is bounded by 2^TAU.
-// - Causal: key blocks entirely above the workgroup's diagonal are never visited; a wave
-//   whose 32 queries all precede a key block skips its math; only blocks that straddle the
-//   diagonal are masked element by element. Each head's query blocks are walked heaviest
-//   first, and the XCD-aware remap keeps a head's blocks on one XCD (one L2).
+// - Causal: key blocks entirely above the workgroup's diagonal are never visited; only
+//   blocks that straddle the diagonal are masked element by element. Each head's query
+//   blocks are walked heaviest first, and the XCD-aware remap keeps a head's blocks on one
+//   XCD (one L2).
 //
 // FP8 inputs ("FlashAttention-3: How Warp Specialization ...", section 4 "Technique 3";
 // "FlashAttention 2 & 3", section "What stays in higher precision"):
@@ -40,6 +46,8 @@
 //   output error on inputs with outliers is an order of magnitude above the 6e-2 budget.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -48,24 +56,37 @@ enum class InKind { BF16, FP8 };
 
 constexpr int kBR = 128;        // queries per workgroup
 constexpr int kThreads = 256;   // 4 waves
+// buffer resource word 3 for raw (untyped) 32-bit-offset buffer loads on gfx950
+constexpr int kBufferConfig = 0x00020000;
 
 template <InKind KIND, int D, int BC>
 struct FwdCfg {
     static constexpr bool F8 = KIND == InKind::FP8;
     static constexpr int IN_BYTES = F8 ? 1 : 2;            // bytes per element in HBM
-    static constexpr int ROW_BYTES = D * IN_BYTES;          // bytes per K/V row in HBM
-    static constexpr int KP = ROW_BYTES + 16;               // LDS pitch of K rows (bytes): 4-bank shift
-    static constexpr int VP = D + 16;                       // LDS pitch of bf16 V rows (elements): 8-bank shift
+    static constexpr int ROW_BYTES = D * IN_BYTES;          // bytes per K row (HBM and LDS)
+    static constexpr int KCPR = ROW_BYTES / 16;             // 16-byte chunks per K row
+    static constexpr int VROW_BYTES = D * 2;                // bytes per bf16 V row in LDS
+    static constexpr int VCPR = VROW_BYTES / 16;
     static constexpr int QK_K = F8 ? 64 : 16;               // contraction length of one QK MFMA
     static constexpr int KSTEPS = D / QK_K;
     static constexpr int MT = BC / 32;                      // 32-key tiles per block
     static constexpr int DT = D / 32;                       // 32-wide d tiles of O^T
     static constexpr int CH = BC / 16;                      // 16-key chunks of the PV product
-    static constexpr int CPT = BC * ROW_BYTES / 16 / kThreads;   // 16-byte chunks per thread per tensor
-    static_assert(CPT >= 1 && CPT * kThreads * 16 == BC * ROW_BYTES, "tile must split evenly");
-    static constexpr int K_BYTES = BC * KP;
-    static constexpr int V_BYTES = BC * VP * 2;
+    static constexpr int K_BYTES = BC * ROW_BYTES;
+    static constexpr int V_BYTES = BC * VROW_BYTES;
+    static constexpr int K_LOADS = K_BYTES / 16 / kThreads;            // direct loads per thread
+    static constexpr int V_LOADS = F8 ? BC * D / 16 / kThreads : V_BYTES / 16 / kThreads;
+    static_assert(K_LOADS >= 1 && K_LOADS * kThreads * 16 == K_BYTES, "K tile must split evenly");
+    static_assert(V_LOADS >= 1, "V tile must split evenly");
+    static constexpr int KSWZ = (KCPR < 16 ? KCPR : 16) - 1;   // XOR mask of the K swizzle
+    static constexpr int VSWZ = VCPR - 1;
 };
+
+// swizzled 16-byte chunk position of chunk c in K row r / bf16 V row r
+template <int MASK>
+__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (swap_bits23(r) & MASK); }
+template <int MASK>
+__device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((2 * (r & 3) ^ 8 * (r & 1)) & MASK); }
 
 template <InKind KIND>
 struct QOperand;
@@ -74,7 +95,12 @@ struct QOperand<InKind::BF16> { typedef bf16x8 type; };
 template <>
 struct QOperand<InKind::FP8> { typedef i32x8 type; };
 
-template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB>
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// PIPE: compute the scores of block j+1 while the softmax of block j runs (needs registers
+// for two score tiles); without it each block's scores are computed just before its softmax.
+template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB, bool PIPE>
 __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
@@ -82,8 +108,8 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     using C = FwdCfg<KIND, D, BC>;
     using QT = typename QOperand<KIND>::type;
     constexpr float tau = (float)TAU;
-    __shared__ __attribute__((aligned(16))) uint8_t smK[2][C::K_BYTES];
-    __shared__ __attribute__((aligned(16))) bf16_t smV[2][BC * C::VP];
+    __shared__ __attribute__((aligned(1024))) uint8_t smK[2][C::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smV[2][C::V_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -103,6 +129,11 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     const uint8_t* Qh = (const uint8_t*)Qv + head_off * C::IN_BYTES;
     const uint8_t* Kh = (const uint8_t*)Kv + head_off * C::IN_BYTES;
     const uint8_t* Vh = (const uint8_t*)Vv + head_off * C::IN_BYTES;
+    // buffer resources over this head's K and V: reads past row N return zero
+    const __amdgpu_buffer_rsrc_t rK =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * C::ROW_BYTES, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rV =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, N * C::ROW_BYTES, kBufferConfig);
 
     const int nkb_all = (N + BC - 1) / BC;
     int nkb = nkb_all;
@@ -139,174 +170,240 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         }
     }
 
-    // ---- K/V staging: each thread moves CPT 16-byte chunks of K and of V per block
-    i32x4 kst[C::CPT], vst[C::CPT];
-    auto load_tile = [&](int kb) {
+    // ---- per-thread source offsets of the direct-to-LDS tile loads. Load i of wave w fills
+    // LDS chunks [64 (K_LOADS w + i), +64): lane L writes chunk p = 64 (K_LOADS w + i) + L,
+    // i.e. row p / CPR, swizzled slot p % CPR, so it fetches source chunk slot ^ f(row).
+    int koff[C::K_LOADS];
 #pragma unroll
-        for (int r = 0; r < C::CPT; ++r) {
-            const int x = tid + kThreads * r;
-            const int row = x / (C::ROW_BYTES / 16);
-            const int c16 = x % (C::ROW_BYTES / 16);
-            const int grow = kb + row;
-            if (grow < N) {
-                kst[r] = *(const i32x4*)(Kh + (size_t)grow * C::ROW_BYTES + 16 * c16);
-                vst[r] = *(const i32x4*)(Vh + (size_t)grow * C::ROW_BYTES + 16 * c16);
-            } else {
-                kst[r] = i32x4{};
-                vst[r] = i32x4{};
-            }
+    for (int i = 0; i < C::K_LOADS; ++i) {
+        const int p = 64 * (C::K_LOADS * wave + i) + lane;
+        const int r = p / C::KCPR;
+        koff[i] = r * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(r, p % C::KCPR);
+    }
+    int voff[C::V_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::V_LOADS; ++i) {
+        if constexpr (C::F8) {
+            // register-staged: thread loads e4m3 chunk x (16 values) of the block
+            const int x = tid + kThreads * i;
+            voff[i] = (x / (D / 16)) * C::ROW_BYTES + 16 * (x % (D / 16));
+        } else {
+            const int p = 64 * (C::V_LOADS * wave + i) + lane;
+            const int r = p / C::VCPR;
+            voff[i] = r * C::ROW_BYTES + 16 * v_slot<C::VSWZ>(r, p % C::VCPR);
+        }
+    }
+    auto load_k = [&](int kb, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < C::K_LOADS; ++i)
+            lds_dma16(rK, dst + 1024 * (C::K_LOADS * wave + i), koff[i] + kb * C::ROW_BYTES);
+    };
+    i32x4 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
+    auto load_v = [&](int kb, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < C::V_LOADS; ++i) {
+            if constexpr (C::F8)
+                vst[i] = buffer_load16(rV, voff[i] + kb * C::ROW_BYTES);
+            else
+                lds_dma16(rV, dst + 1024 * (C::V_LOADS * wave + i), voff[i] + kb * C::ROW_BYTES);
         }
     };
-    auto store_tile = [&](int buf) {
+    // FP8: expand the staged e4m3 V chunks exactly to bf16 and store them swizzled
+    auto store_v = [&](uint8_t* dst) {
+        if constexpr (C::F8) {
 #pragma unroll
-        for (int r = 0; r < C::CPT; ++r) {
-            const int x = tid + kThreads * r;
-            const int row = x / (C::ROW_BYTES / 16);
-            const int c16 = x % (C::ROW_BYTES / 16);
-            *(i32x4*)(&smK[buf][row * C::KP + 16 * c16]) = kst[r];
-            if constexpr (C::F8) {
-                // 16 e4m3 values -> 16 bf16 values, exact (the convert's scale operand only
-                // contributes its power of two, so it is left at 1 and s_V is applied to P)
+            for (int i = 0; i < C::V_LOADS; ++i) {
+                const int x = tid + kThreads * i;
+                const int r = x / (D / 16);
+                const int c8 = x % (D / 16);   // 16 e4m3 values = bf16 chunks 2 c8 and 2 c8 + 1
                 i32x4 lo, hi;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[r][u], 1.f, false);
-                    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[r][u], 1.f, true);
-                    const int wa = __builtin_bit_cast(int, a);
-                    const int wb = __builtin_bit_cast(int, b);
+                    const int wa = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[i][u], 1.f, false));
+                    const int wb = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[i][u], 1.f, true));
                     if (u < 2) { lo[2 * u] = wa; lo[2 * u + 1] = wb; }
                     else { hi[2 * (u - 2)] = wa; hi[2 * (u - 2) + 1] = wb; }
                 }
-                *(i32x4*)(&smV[buf][row * C::VP + 16 * c16]) = lo;
-                *(i32x4*)(&smV[buf][row * C::VP + 16 * c16 + 8]) = hi;
-            } else {
-                *(i32x4*)(&smV[buf][row * C::VP + 8 * c16]) = vst[r];
+                *(i32x4*)(dst + r * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(r, 2 * c8)) = lo;
+                *(i32x4*)(dst + r * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(r, 2 * c8 + 1)) = hi;
             }
         }
     };
 
-    // ---- online-softmax state (log2 domain: m is a running max of S * scale * log2 e)
+    // ---- per-lane LDS read addresses (relative to a tile buffer). The swizzles only touch
+    // the low 4 bits of a chunk index, so chunks 16 apart keep a fixed 256-byte distance and
+    // only the first 16 chunks of a row need a per-lane address.
+    // K operand of QK step s, 32-key tile t: row 32t + swap_bits23(col), chunk c(s, h)
+    constexpr int KREADS = C::F8 ? 2 : 1;              // 16-byte reads per operand
+    constexpr int KSPAN = C::F8 ? 4 : 8;               // steps per 16 chunks
+    constexpr int KA = C::KSTEPS < KSPAN ? C::KSTEPS : KSPAN;
+    int kaddr[KA][KREADS];
+    {
+        const int rr = swap_bits23(col);   // same swizzle for rows rr and 32t + rr
+#pragma unroll
+        for (int s = 0; s < KA; ++s)
+#pragma unroll
+            for (int u = 0; u < KREADS; ++u) {
+                const int c = C::F8 ? 4 * s + 2 * h + u : 2 * s + h;
+                kaddr[s][u] = rr * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(rr, c);
+            }
+    }
+    // V^T operand of PV chunk ch, d tile e: rows 16ch + 8(g>>1) + (L>>2) (+4), the 8 bytes
+    // of columns 32e + 16(g&1) + 4(L&3) .. +3. The swizzle depends on row & 3 = (L>>2) only.
+    constexpr int VA = C::DT < 4 ? C::DT : 4;          // 4 d tiles = 16 chunks
+    int vaddr[VA];
+    {
+        const int g = lane >> 4, L = lane & 15;
+        const int vr = 8 * (g >> 1) + (L >> 2);
+#pragma unroll
+        for (int e = 0; e < VA; ++e) {
+            const int byte = 64 * e + 32 * (g & 1) + 8 * (L & 3);
+            vaddr[e] = vr * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(vr, byte / 16) + (byte & 15);
+        }
+    }
+
+    // ---- state
     f32x16 acc[C::DT];
 #pragma unroll
     for (int e = 0; e < C::DT; ++e) acc[e] = f32x16{};
     float m_run = -INFINITY;
     float l_run = 0.f;
+    // result register i = 4a + b of a 32-key tile holds key swap_bits23(8a + 4h + b)
+    //                                                     = 16(a>>1) + 4(a&1) + b + 8h
+    const int key8h = 8 * h;
+    f32x16 s_buf[PIPE ? 2 : 1][C::MT];   // scores of blocks j (index j&1) and j+1
 
-    // per-lane key offsets of the 16 result registers within a 32-key tile
-    int koff[16];
+    auto qk = [&](const uint8_t* kt, f32x16* st) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) koff[i] = swap_bits23(mfma32_row(i, h));
-    const int krow_a = swap_bits23(col);   // key row this lane feeds into A-operand row `col`
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int j = 0; j < nkb; ++j) {
-        const int buf = j & 1;
-        const int kb = j * BC;
-        if (j + 1 < nkb) load_tile(kb + BC);
-
-        const bool active = (q0w < N) && (!CAUSAL || kb <= q0w + 31);
-        if (active) {
-            const uint8_t* sk = smK[buf];
-            const bf16_t* sv = smV[buf];
-            // ---- S^T = K_j Q_i^T
-            f32x16 st[C::MT];
+        for (int t = 0; t < C::MT; ++t) st[t] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
             for (int t = 0; t < C::MT; ++t) {
-                st[t] = f32x16{};
-                const uint8_t* kp = sk + (32 * t + krow_a) * C::KP + (C::QK_K / 2) * C::IN_BYTES * h;
-#pragma unroll
-                for (int s = 0; s < C::KSTEPS; ++s) {
-                    const uint8_t* p = kp + s * C::QK_K * C::IN_BYTES;
-                    if constexpr (C::F8) {
-                        const i32x4 lo = *(const i32x4*)p;
-                        const i32x4 hi = *(const i32x4*)(p + 16);
-                        const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], st[t], 0, 0, 0, 127, 0,
-                                                                                 127);
-                    } else {
-                        const bf16x8 a = *(const bf16x8*)p;
-                        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[t], 0, 0, 0);
-                    }
+                const uint8_t* p = kt + 32 * t * C::ROW_BYTES + 256 * (s / KSPAN);
+                if constexpr (C::F8) {
+                    const i32x4 lo = *(const i32x4*)(p + kaddr[s % KSPAN][0]);
+                    const i32x4 hi = *(const i32x4*)(p + kaddr[s % KSPAN][KREADS - 1]);
+                    const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], st[t], 0, 0, 0, 127, 0, 127);
+                } else {
+                    const bf16x8 a = *(const bf16x8*)(p + kaddr[s % KSPAN][0]);
+                    st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[t], 0, 0, 0);
                 }
             }
-            float ct = cq;
-            if constexpr (C::F8) ct *= SK[(size_t)bh * nsb + j];
-            // ---- masks: ragged tail of keys, causal diagonal
-            const bool need_mask = (kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w);
-            if (need_mask) {
-#pragma unroll
-                for (int t = 0; t < C::MT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb + 32 * t + koff[i];
-                        const bool hide = (key >= N) || (CAUSAL && key > qrow);
-                        if (hide) st[t][i] = -INFINITY;
-                    }
-            }
-            // ---- block row max, conditional rescale
-            float mx = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < C::MT; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][i]);
-            mx = pair_max(mx) * ct;
-            const float m_new = fmaxf(m_run, mx);
-            const bool grow = m_new > m_run + tau;
-            if (wave_any(grow)) {
-                const float m_ref = grow ? m_new : m_run;
-                const float alpha = (m_ref == -INFINITY) ? 1.f : fast_exp2(m_run - m_ref);
-                m_run = m_ref;
-                l_run *= alpha;
-#pragma unroll
-                for (int e = 0; e < C::DT; ++e)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[e][i] *= alpha;
-            }
-            // ---- P = exp2(S ct - m), partial row sums, bf16 operand of the PV product
-            // (FP8: P carries r = s_V(j) / max s_V, divided back out of the row sum)
-            float bias = (m_run == -INFINITY) ? 0.f : -m_run;
-            float inv_r = 1.f;
-            if constexpr (C::F8) {
-                const float r = SV[(size_t)bh * nsb + j] / svmax;
-                bias += __log2f(r);
-                inv_r = svmax / SV[(size_t)bh * nsb + j];
-            }
-            bf16x8 pf[C::CH];
-            float lsum = 0.f;
+    };
+
+    // one key block j (buffer parity B): softmax of s_cur (block j) overlapped with the
+    // scores of block j+1 (if NEXT), then O += P_j V_j
+    auto step = [&](int j, auto b_c, auto next_c) {
+        constexpr int B = decltype(b_c)::value;
+        constexpr bool NEXT = decltype(next_c)::value != 0;
+        f32x16* s_cur = s_buf[PIPE ? B : 0];
+        f32x16* s_nxt = s_buf[PIPE ? (B ^ 1) : 0];
+        const int kb = j * BC;
+        // issue the loads of the next blocks: K_{j+2} into K_j's buffer (K_{j+1} without the
+        // pipeline) and V_{j+1}
+        if constexpr (PIPE) {
+            if (j + 2 < nkb) load_k(kb + 2 * BC, smK[B]);
+        } else {
+            if (NEXT) load_k(kb + BC, smK[B ^ 1]);
+        }
+        if (NEXT) load_v(kb + BC, smV[B ^ 1]);
+        if constexpr (!PIPE) qk(smK[B], s_cur);
+
+        float ct = cq;
+        if constexpr (C::F8) ct *= SK[(size_t)bh * nsb + j];
+        // masks: ragged tail of keys, causal diagonal
+        if ((kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w)) {
 #pragma unroll
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(__builtin_fmaf(st[t][i], ct, bias));
-                    lsum += p;
-                    pf[2 * t + i / 8][i % 8] = (bf16_t)p;
+                    const int key = kb + key8h + 32 * t + 16 * ((i >> 2) >> 1) + 4 * ((i >> 2) & 1) + (i & 3);
+                    if ((key >= N) || (CAUSAL && key > qrow)) s_cur[t][i] = -INFINITY;
                 }
-            if constexpr (C::F8) lsum *= inv_r;
-            l_run += lsum;
-            // ---- O^T += V_j^T P^T : A = V^T (d rows x 16 keys) via transposing LDS reads
-            const int g = lane >> 4;       // 16-lane group
-            const int L = lane & 15;
-            const int vrow = 8 * (g >> 1) + (L >> 2);
-            const int vcol = 16 * (g & 1) + 4 * (L & 3);
-#pragma unroll
-            for (int ch = 0; ch < C::CH; ++ch) {
-#pragma unroll
-                for (int e = 0; e < C::DT; ++e) {
-                    const bf16_t* vp = sv + (16 * ch + vrow) * C::VP + 32 * e + vcol;
-                    // keys 16ch + 8h + 0..3 and + 4..7 of column d, concatenated as whole vectors
-                    // (element-wise assembly of the two halves is mis-compiled by the toolchain)
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp));
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp + 4 * C::VP));
-                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], acc[e], 0, 0, 0);
-                }
-            }
         }
-        if (j + 1 < nkb) store_tile(buf ^ 1);
+        // ---- phase A: scores of block j+1 on the matrix cores, softmax of block j on the VALU
+        if constexpr (PIPE && NEXT) qk(smK[B ^ 1], s_nxt);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[t][i]);
+        mx = pair_max(mx) * ct;
+        const float m_new = fmaxf(m_run, mx);
+        const bool grow = m_new > m_run + tau;
+        const float m_ref = grow ? m_new : m_run;
+        const float alpha = (grow && m_run != -INFINITY) ? fast_exp2(m_run - m_ref) : (grow ? 0.f : 1.f);
+        m_run = m_ref;
+        float bias = (m_run == -INFINITY) ? 0.f : -m_run;
+        float inv_r = 1.f;
+        if constexpr (C::F8) {
+            const float sv = SV[(size_t)bh * nsb + j];
+            bias += __log2f(sv / svmax);
+            inv_r = svmax / sv;
+        }
+        bf16x8 pf[C::CH];
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(__builtin_fmaf(s_cur[t][i], ct, bias));
+                lsum += p;
+                pf[2 * t + i / 8][i % 8] = (bf16_t)p;
+            }
+        if constexpr (C::F8) lsum *= inv_r;
+        l_run = l_run * alpha + lsum;
+        // ---- rescale the accumulator (rare with TAU > 0)
+        if (wave_any(grow)) {
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[e][i] *= alpha;
+        }
+        // ---- phase B: O^T += V_j^T P_j^T
+        const uint8_t* vt = smV[B];
+#pragma unroll
+        for (int ch = 0; ch < C::CH; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e) {
+                const uint8_t* vp = vt + 16 * ch * C::VROW_BYTES + 256 * (e / 4) + vaddr[e % 4];
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp + 4 * C::VROW_BYTES));
+                // concatenated as whole vectors (element-wise assembly is mis-compiled)
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], acc[e], 0, 0, 0);
+            }
+        if constexpr (C::F8) {
+            if (NEXT) store_v(smV[B ^ 1]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    // ---- prologue: K_0, V_0 (and K_1, S_0 with the pipeline)
+    load_k(0, smK[0]);
+    load_v(0, smV[0]);
+    if (PIPE && nkb > 1) load_k(BC, smK[1]);
+    __builtin_amdgcn_s_waitcnt(0);
+    store_v(smV[0]);
+    __syncthreads();
+    if constexpr (PIPE) {
+        qk(smK[0], s_buf[0]);
+        __syncthreads();   // every wave is done with smK[0] before block 0 refills it
+    }
+
+    int j = 0;
+    for (; j + 2 < nkb; j += 2) {
+        step(j, IC<0>{}, IC<1>{});
+        step(j + 1, IC<1>{}, IC<1>{});
+    }
+    if (j + 1 < nkb) {
+        step(j, IC<0>{}, IC<1>{});
+        step(j + 1, IC<1>{}, IC<0>{});
+    } else {
+        step(j, IC<0>{}, IC<0>{});
     }
 
     // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2
@@ -328,14 +425,14 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     }
 }
 
-template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB>
+template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB, bool PIPE = (D <= 128)>
 hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const float* sq, const float* sk,
                              const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream) {
     const int numQB = (N + kBR - 1) / kBR;
     const int nsb = (N + 63) / 64;
     const long long total = (long long)BH * numQB;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, CAUSAL, TAU, MINB>), dim3((unsigned)total), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, CAUSAL, TAU, MINB, PIPE>), dim3((unsigned)total), dim3(kThreads), 0,
                        stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e);
     return hipGetLastError();
 }
