@@ -121,6 +121,27 @@ hipError_t launch_prep(const float* x, void* x8, float* s, const float* signs, i
     return hipGetLastError();
 }
 
+#ifndef FA_F8_D128_NQ
+#define FA_F8_D128_NQ 1
+#endif
+#ifndef FA_F8_D128_BC
+#define FA_F8_D128_BC 32
+#endif
+#ifndef FA_F8_D128_MINB
+#define FA_F8_D128_MINB (FA_F8_D128_NQ == 2 ? 1 : 2)
+#endif
+
+template <int D, int BC, int NQ, int MINB, bool PIPE>
+hipError_t dispatch_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
+                        const float* sv, void* o, float* lse, int BH, int N, float scale, bool causal,
+                        hipStream_t stream) {
+    constexpr InKind K = InKind::FP8;
+    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale,
+                                                                         stream)
+                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale,
+                                                                          stream);
+}
+
 }  // namespace
 
 hipError_t launch_prep_fp8(const float* x, void* x8, float* s, const float* signs, int BH, int N, int d,
@@ -136,20 +157,13 @@ hipError_t launch_prep_fp8(const float* x, void* x8, float* s, const float* sign
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                           const float* sv, void* o, float* lse, int BH, int N, int d, float scale, bool causal,
                           hipStream_t stream) {
-    // 64-key blocks (one scale block each); conditional rescale threshold 2^8
-    constexpr InKind K = InKind::FP8;
+    // key blocks of 64 keys (one scale block) or, for d = 128, 32 (half of one; fewer live
+    // registers, as for bf16); conditional rescale threshold 2^8
     switch (d) {
-        case 64:
-            return causal ? launch_fwd_kernel<K, 64, 64, true, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream)
-                          : launch_fwd_kernel<K, 64, 64, false, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream);
-        case 128:
-            return causal ? launch_fwd_kernel<K, 128, 64, true, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream)
-                          : launch_fwd_kernel<K, 128, 64, false, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream);
-        case 256:
-            return causal ? launch_fwd_kernel<K, 256, 64, true, 8, 1>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream)
-                          : launch_fwd_kernel<K, 256, 64, false, 8, 1>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream);
-        default:
-            return hipErrorInvalidValue;
+        case 64: return dispatch_fp8<64, 64, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        case 128: return dispatch_fp8<128, FA_F8_D128_BC, FA_F8_D128_NQ, FA_F8_D128_MINB, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        case 256: return dispatch_fp8<256, 64, 1, 1, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

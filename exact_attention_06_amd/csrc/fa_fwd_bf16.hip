@@ -1,31 +1,54 @@
 // bf16 attention forward: instances of the shared fused kernel (fa_fwd_kernel.h) for
 // bfloat16 Q, K, V and O, with the conditional-rescale threshold 2^8.
+//
+// Tile choices per head dimension (keys per block BC, 32-query tiles per wave NQ,
+// workgroups per CU MINB, score pipeline PIPE):
+//   d =  64: BC 64, NQ 1, 2 workgroups per CU, pipelined
+//   d = 128: BC 32, NQ 1, 2 workgroups per CU, pipelined (BC 64 needs more registers than
+//            two workgroups per CU leave, and the spill reloads stall on the tile loads in
+//            flight, since vector-memory counters retire in order). (NQ 2 halves the LDS operand
+//            traffic per FLOP but needs one wave per SIMD with 512 registers; the compiler
+//            then spills and copies between register files, and it measured ~40% slower.)
+//   d = 256: BC 32, NQ 1, one workgroup per CU, not pipelined (registers)
 #include "fa_fwd_kernel.h"
 #include "fa_internal.h"
 
+#ifndef FA_D128_NQ
+#define FA_D128_NQ 1
+#endif
+#ifndef FA_D128_BC
+#define FA_D128_BC 32
+#endif
+#ifndef FA_D128_MINB
+#define FA_D128_MINB (FA_D128_NQ == 2 ? 1 : 2)
+#endif
+#ifndef FA_D128_PIPE
+#define FA_D128_PIPE 1
+#endif
+
 namespace fa {
+namespace {
+
+template <int D, int BC, int NQ, int MINB, bool PIPE>
+hipError_t dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float scale,
+                    bool causal, hipStream_t stream) {
+    constexpr InKind K = InKind::BF16;
+    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE>(q, k, v, nullptr, nullptr, nullptr, o, lse,
+                                                                         BH, N, scale, stream)
+                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE>(q, k, v, nullptr, nullptr, nullptr, o, lse,
+                                                                          BH, N, scale, stream);
+}
+
+}  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream) {
-    constexpr InKind K = InKind::BF16;
     switch (d) {
-        case 64:
-            return causal ? launch_fwd_kernel<K, 64, 64, true, 8, 2>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH, N,
-                                                                     scale, stream)
-                          : launch_fwd_kernel<K, 64, 64, false, 8, 2>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH,
-                                                                      N, scale, stream);
+        case 64: return dispatch<64, 64, 1, 2, true>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 128:
-            return causal ? launch_fwd_kernel<K, 128, 64, true, 8, 2>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH,
-                                                                      N, scale, stream)
-                          : launch_fwd_kernel<K, 128, 64, false, 8, 2>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH,
-                                                                       N, scale, stream);
-        case 256:
-            return causal ? launch_fwd_kernel<K, 256, 32, true, 8, 1>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH,
-                                                                      N, scale, stream)
-                          : launch_fwd_kernel<K, 256, 32, false, 8, 1>(q, k, v, nullptr, nullptr, nullptr, o, lse, BH,
-                                                                       N, scale, stream);
-        default:
-            return hipErrorInvalidValue;
+            return dispatch<128, FA_D128_BC, FA_D128_NQ, FA_D128_MINB, FA_D128_PIPE != 0>(q, k, v, o, lse, BH, N, scale, causal, stream);
+        case 256: return dispatch<256, 32, 1, 1, false>(q, k, v, o, lse, BH, N, scale, causal, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

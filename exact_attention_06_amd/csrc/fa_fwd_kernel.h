@@ -35,9 +35,9 @@
 //
 // FP8 inputs ("FlashAttention-3: How Warp Specialization ...", section 4 "Technique 3";
 // "FlashAttention 2 & 3", section "What stays in higher precision"):
-// - Q8 and K8 are e4m3 with one fp32 scale per 64 rows; 64-key blocks match the scale
-//   blocks, so the score of the block is s_Q s_K (Q8 K8^T) and s_Q s_K is folded into the
-//   FMA that subtracts the running max;
+// - Q8 and K8 are e4m3 with one fp32 scale per 64 rows; a key block (32 or 64 keys) and a
+//   32-query tile each lie inside one scale block, so the score of the block is
+//   s_Q s_K (Q8 K8^T) and s_Q s_K is folded into the FMA that subtracts the running max;
 // - V stays e4m3 in HBM and is expanded exactly to bf16 when it is written to LDS (every
 //   e4m3 value is a bf16 value); its block scale rides on P: P_j is computed as
 //   exp2(S ct - m + log2(s_V(j) / max s_V)) in the same FMA (no extra per-element work),
@@ -54,7 +54,6 @@ namespace fa {
 
 enum class InKind { BF16, FP8 };
 
-constexpr int kBR = 128;        // queries per workgroup
 constexpr int kThreads = 256;   // 4 waves
 // buffer resource word 3 for raw (untyped) 32-bit-offset buffer loads on gfx950
 constexpr int kBufferConfig = 0x00020000;
@@ -78,6 +77,8 @@ struct FwdCfg {
     static constexpr int V_LOADS = F8 ? BC * D / 16 / kThreads : V_BYTES / 16 / kThreads;
     static_assert(K_LOADS >= 1 && K_LOADS * kThreads * 16 == K_BYTES, "K tile must split evenly");
     static_assert(V_LOADS >= 1, "V tile must split evenly");
+    // FP8: a key block lies inside one 64-row scale block of K and V
+    static_assert(!F8 || 64 % BC == 0, "FP8 key blocks must divide the 64-row scale blocks");
     static constexpr int KSWZ = (KCPR < 16 ? KCPR : 16) - 1;   // XOR mask of the K swizzle
     static constexpr int VSWZ = VCPR - 1;
 };
@@ -98,9 +99,11 @@ struct QOperand<InKind::FP8> { typedef i32x8 type; };
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// NQ: 32-query tiles per wave (the workgroup owns 4 * 32 * NQ queries). With NQ = 2 every K
+// and V^T operand read from LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
 // PIPE: compute the scores of block j+1 while the softmax of block j runs (needs registers
 // for two score tiles); without it each block's scores are computed just before its softmax.
-template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB, bool PIPE>
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE>
 __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
@@ -108,22 +111,31 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     using C = FwdCfg<KIND, D, BC>;
     using QT = typename QOperand<KIND>::type;
     constexpr float tau = (float)TAU;
-    __shared__ __attribute__((aligned(1024))) uint8_t smK[2][C::K_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t smV[2][C::V_BYTES];
+    constexpr int BR = 4 * 32 * NQ;   // queries per workgroup
+    // separate objects per buffer, so that the compiler can tell that LDS reads of one
+    // buffer do not depend on the DMA writes still in flight into the other one
+    __shared__ __attribute__((aligned(1024))) uint8_t smK0[C::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smK1[C::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smV0[C::V_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smV1[C::V_BYTES];
+    uint8_t* const smK[2] = {smK0, smK1};
+    uint8_t* const smV[2] = {smV0, smV1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int h = lane >> 5;        // lane half
-    const int col = lane & 31;      // query column owned by this lane
+    const int col = lane & 31;      // query column owned by this lane in each query tile
 
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = w / numQB;
     const int qi = w - bh * numQB;
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
-    const int q0 = qb * kBR;
-    const int q0w = q0 + wave * 32;
-    const int qrow = q0w + col;
+    const int q0 = qb * BR;
+    const int q0w = q0 + wave * 32 * NQ;
+    int qrow[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) qrow[n] = q0w + 32 * n + col;
 
     const size_t head_off = (size_t)bh * N * D;   // elements
     const uint8_t* Qh = (const uint8_t*)Qv + head_off * C::IN_BYTES;
@@ -137,75 +149,90 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
 
     const int nkb_all = (N + BC - 1) / BC;
     int nkb = nkb_all;
-    if (CAUSAL) nkb = min(nkb_all, (min(q0 + kBR, N) - 1) / BC + 1);
+    if (CAUSAL) nkb = min(nkb_all, (min(q0 + BR, N) - 1) / BC + 1);
 
-    // score scale (log2 units); FP8 adds the Q block scale of this wave
-    float cq = c2;
+    // score scale (log2 units); FP8 adds the Q block scale of each query tile
+    float cq[NQ];
     float svmax = 1.f;   // FP8: largest V block scale of this head
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) cq[n] = c2;
     if constexpr (C::F8) {
-        cq *= (q0w < N) ? SQ[(size_t)bh * nsb + q0w / 64] : 1.f;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int qt0 = q0w + 32 * n;
+            cq[n] *= (qt0 < N) ? SQ[(size_t)bh * nsb + qt0 / 64] : 1.f;
+        }
         float mx = 0.f;
-        for (int i = lane; i < nkb_all; i += kWave) mx = fmaxf(mx, SV[(size_t)bh * nsb + i]);
+        for (int i = lane; i < nsb; i += kWave) mx = fmaxf(mx, SV[(size_t)bh * nsb + i]);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
         svmax = mx;
     }
 
-    // ---- Q^T operand (B of S^T = K Q^T): lane holds query `qrow`; step s covers head-dim
-    // elements [QK_K s + (QK_K/2) h, +QK_K/2)
-    QT qf[C::KSTEPS];
-    {
-        const bool ok = qrow < N;
-        const uint8_t* qp = Qh + (size_t)(ok ? qrow : 0) * C::ROW_BYTES + (C::QK_K / 2) * C::IN_BYTES * h;
+    // ---- Q^T operands (B of S^T = K Q^T): in tile n the lane holds query qrow[n]; step s
+    // covers head-dim elements [QK_K s + (QK_K/2) h, +QK_K/2)
+    QT qf[NQ][C::KSTEPS];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const bool ok = qrow[n] < N;
+        const uint8_t* qp = Qh + (size_t)(ok ? qrow[n] : 0) * C::ROW_BYTES + (C::QK_K / 2) * C::IN_BYTES * h;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
             const uint8_t* p = qp + s * C::QK_K * C::IN_BYTES;
             if constexpr (C::F8) {
                 const i32x4 lo = ok ? *(const i32x4*)p : i32x4{};
                 const i32x4 hi = ok ? *(const i32x4*)(p + 16) : i32x4{};
-                qf[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                qf[n][s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             } else {
-                qf[s] = ok ? *(const bf16x8*)p : bf16x8{};
+                qf[n][s] = ok ? *(const bf16x8*)p : bf16x8{};
             }
         }
     }
 
-    // ---- per-thread source offsets of the direct-to-LDS tile loads. Load i of wave w fills
-    // LDS chunks [64 (K_LOADS w + i), +64): lane L writes chunk p = 64 (K_LOADS w + i) + L,
-    // i.e. row p / CPR, swizzled slot p % CPR, so it fetches source chunk slot ^ f(row).
-    int koff[C::K_LOADS];
+    // ---- per-thread source offsets of the direct-to-LDS tile loads. One load instruction of
+    // a wave fills one 1 KB region of the tile (RPL rows); load i of wave w fills region
+    // w + 4 i: lane L writes row RPL (w + 4 i) + L / CPR, swizzled slot L % CPR, so it fetches
+    // source chunk slot ^ f(row). The rows of one thread's loads are 4 RPL apart; when that is
+    // a multiple of the swizzle period (16 rows for K, 4 for V) every load of the thread has
+    // the same swizzle, and its offsets are one register plus constants (fewer live VGPRs).
+    constexpr int KRPL = 1024 / C::ROW_BYTES;
+    constexpr bool KUNI = (4 * KRPL) % 16 == 0;
+    constexpr int KN = KUNI ? 1 : C::K_LOADS;
+    int koff[KN];
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-        const int p = 64 * (C::K_LOADS * wave + i) + lane;
-        const int r = p / C::KCPR;
-        koff[i] = r * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(r, p % C::KCPR);
+    for (int i = 0; i < KN; ++i) {
+        const int r = KRPL * (wave + 4 * i) + lane / C::KCPR;
+        koff[i] = r * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(r, lane % C::KCPR);
     }
-    int voff[C::V_LOADS];
-#pragma unroll
-    for (int i = 0; i < C::V_LOADS; ++i) {
-        if constexpr (C::F8) {
-            // register-staged: thread loads e4m3 chunk x (16 values) of the block
-            const int x = tid + kThreads * i;
-            voff[i] = (x / (D / 16)) * C::ROW_BYTES + 16 * (x % (D / 16));
-        } else {
-            const int p = 64 * (C::V_LOADS * wave + i) + lane;
-            const int r = p / C::VCPR;
-            voff[i] = r * C::ROW_BYTES + 16 * v_slot<C::VSWZ>(r, p % C::VCPR);
-        }
+    auto koff_of = [&](int i) { return KUNI ? koff[0] + 4 * KRPL * C::ROW_BYTES * i : koff[i]; };
+    constexpr int VRPL = 1024 / C::VROW_BYTES;
+    int voff0;
+    if constexpr (C::F8) {
+        // register-staged: load i of a thread reads e4m3 chunk x = tid + 256 i (16 values),
+        // row x / (D/16); 256 is a multiple of D/16, so rows of successive loads are
+        // 256 / (D/16) apart
+        voff0 = (tid / (D / 16)) * C::ROW_BYTES + 16 * (tid % (D / 16));
+    } else {
+        const int r = VRPL * wave + lane / C::VCPR;
+        voff0 = r * C::ROW_BYTES + 16 * v_slot<C::VSWZ>(r, lane % C::VCPR);
     }
+    auto voff_of = [&](int i) {
+        if constexpr (C::F8) return voff0 + (kThreads / (D / 16)) * C::ROW_BYTES * i;
+        return voff0 + 4 * VRPL * C::ROW_BYTES * i;   // rows 4 VRPL apart keep the V swizzle
+    };
     auto load_k = [&](int kb, uint8_t* dst) {
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i)
-            lds_dma16(rK, dst + 1024 * (C::K_LOADS * wave + i), koff[i] + kb * C::ROW_BYTES);
+            lds_dma16(rK, dst + 1024 * (wave + 4 * i), koff_of(i) + kb * C::ROW_BYTES);
     };
     i32x4 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
     auto load_v = [&](int kb, uint8_t* dst) {
 #pragma unroll
         for (int i = 0; i < C::V_LOADS; ++i) {
             if constexpr (C::F8)
-                vst[i] = buffer_load16(rV, voff[i] + kb * C::ROW_BYTES);
+                vst[i] = buffer_load16(rV, voff_of(i) + kb * C::ROW_BYTES);
             else
-                lds_dma16(rV, dst + 1024 * (C::V_LOADS * wave + i), voff[i] + kb * C::ROW_BYTES);
+                lds_dma16(rV, dst + 1024 * (wave + 4 * i), voff_of(i) + kb * C::ROW_BYTES);
         }
     };
     // FP8: expand the staged e4m3 V chunks exactly to bf16 and store them swizzled
@@ -262,20 +289,32 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         }
     }
 
-    // ---- state
-    f32x16 acc[C::DT];
+    // ---- state. The running max starts at a finite sentinel instead of -inf, so that the
+    // rescale factor exp2(m_old - m_new) and the softmax bias need no special cases: a row
+    // that has seen no key yet has l = 0, and masked scores are -inf whatever the bias.
+    constexpr float kNoMax = -1e30f;
+    f32x16 acc[NQ][C::DT];
+    float m_run[NQ], l_run[NQ], alpha[NQ];
+    bool grow[NQ];
 #pragma unroll
-    for (int e = 0; e < C::DT; ++e) acc[e] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+        for (int e = 0; e < C::DT; ++e) acc[n][e] = f32x16{};
+        m_run[n] = kNoMax;
+        l_run[n] = 0.f;
+        alpha[n] = 1.f;
+        grow[n] = false;
+    }
     // result register i = 4a + b of a 32-key tile holds key swap_bits23(8a + 4h + b)
     //                                                     = 16(a>>1) + 4(a&1) + b + 8h
     const int key8h = 8 * h;
-    f32x16 s_buf[PIPE ? 2 : 1][C::MT];   // scores of blocks j (index j&1) and j+1
+    f32x16 s_buf[PIPE ? 2 : 1][C::MT][NQ];   // scores of blocks j (index j&1) and j+1
 
-    auto qk = [&](const uint8_t* kt, f32x16* st) {
+    auto qk = [&](const uint8_t* kt, f32x16 (*st)[NQ]) {
 #pragma unroll
-        for (int t = 0; t < C::MT; ++t) st[t] = f32x16{};
+        for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) st[t][n] = f32x16{};
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
@@ -285,21 +324,71 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
                     const i32x4 lo = *(const i32x4*)(p + kaddr[s % KSPAN][0]);
                     const i32x4 hi = *(const i32x4*)(p + kaddr[s % KSPAN][KREADS - 1]);
                     const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[s], st[t], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int n = 0; n < NQ; ++n)
+                        st[t][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[n][s], st[t][n], 0, 0, 0,
+                                                                                    127, 0, 127);
                 } else {
                     const bf16x8 a = *(const bf16x8*)(p + kaddr[s % KSPAN][0]);
-                    st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[t], 0, 0, 0);
+#pragma unroll
+                    for (int n = 0; n < NQ; ++n)
+                        st[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n][s], st[t][n], 0, 0, 0);
                 }
             }
     };
+    // hide keys past N and, for the causal mask, keys after the query. Called only for
+    // blocks that need it (the diagonal blocks and the ragged last block), unconditionally.
+    // Key kb + 8h + off is visible to query qrow iff off <= lim = (last visible key) - kb - 8h,
+    // with off a compile-time constant per register: one threshold per lane and block.
+    auto mask = [&](f32x16 (*st)[NQ], int kb) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int lim = (CAUSAL ? min(qrow[n], N - 1) : N - 1) - kb - key8h;
+#pragma unroll
+            for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 32 * t + 16 * ((i >> 2) >> 1) + 4 * ((i >> 2) & 1) + (i & 3);
+                    st[t][n][i] = off > lim ? -INFINITY : st[t][n][i];
+                }
+        }
+    };
+    // blocks [0, nfull) need no mask for any query of the workgroup
+    int nfull;
+    if (CAUSAL) nfull = min(N / BC, (q0 + 1) / BC);
+    else nfull = N / BC;
+    auto kscale = [&](int jj) {
+        if constexpr (C::F8) return SK[(size_t)bh * nsb + jj * BC / 64];
+        return 1.f;
+    };
+    // row max of block jj: new reference max (moved only past 2^TAU), rescale factor
+    auto row_max = [&](f32x16 (*st)[NQ], int jj) {
+        const float ks = kscale(jj);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][n][i]);
+            mx = pair_max(mx) * (cq[n] * ks);
+            const float m_new = fmaxf(m_run[n], mx);
+            grow[n] = m_new > m_run[n] + tau;
+            const float m_ref = grow[n] ? m_new : m_run[n];
+            alpha[n] = fast_exp2(m_run[n] - m_ref);
+            m_run[n] = m_ref;
+        }
+    };
 
-    // one key block j (buffer parity B): softmax of s_cur (block j) overlapped with the
-    // scores of block j+1 (if NEXT), then O += P_j V_j
-    auto step = [&](int j, auto b_c, auto next_c) {
+    // one key block j (buffer parity B). With the pipeline one branch-free region holds
+    // [P_j on the VALU | scores of block j+1 on the matrix cores], [O += P_j V_j on the matrix
+    // cores | mask and row max of block j+1 on the VALU]. MASKN: block j+1 needs the mask.
+    auto step = [&](int j, auto b_c, auto next_c, auto maskn_c) {
         constexpr int B = decltype(b_c)::value;
         constexpr bool NEXT = decltype(next_c)::value != 0;
-        f32x16* s_cur = s_buf[PIPE ? B : 0];
-        f32x16* s_nxt = s_buf[PIPE ? (B ^ 1) : 0];
+        constexpr bool MASKN = decltype(maskn_c)::value != 0;
+        auto s_cur = s_buf[PIPE ? B : 0];
+        auto s_nxt = s_buf[PIPE ? (B ^ 1) : 0];
         const int kb = j * BC;
         // issue the loads of the next blocks: K_{j+2} into K_j's buffer (K_{j+1} without the
         // pipeline) and V_{j+1}
@@ -309,60 +398,55 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
             if (NEXT) load_k(kb + BC, smK[B ^ 1]);
         }
         if (NEXT) load_v(kb + BC, smV[B ^ 1]);
-        if constexpr (!PIPE) qk(smK[B], s_cur);
-
-        float ct = cq;
-        if constexpr (C::F8) ct *= SK[(size_t)bh * nsb + j];
-        // masks: ragged tail of keys, causal diagonal
-        if ((kb + BC > N) || (CAUSAL && kb + BC - 1 > q0w)) {
+        if constexpr (!PIPE) {
+            qk(smK[B], s_cur);
+            if (j >= nfull) mask(s_cur, kb);
+            row_max(s_cur, j);
+        }
+        // ---- rescale the accumulators for block j's reference max (rare with TAU > 0)
+        bool any_grow = false;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            l_run[n] *= alpha[n];
+            any_grow = any_grow || grow[n];
+        }
+        if (wave_any(any_grow)) {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n)
+#pragma unroll
+                for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[n][e][i] *= alpha[n];
+        }
+        // ---- P_j = exp2(S_j ct - m) (FP8: times s_V(j) / max s_V)
+        float lbias = 0.f;
+        float inv_r = 1.f;
+        if constexpr (C::F8) {
+            const float sv = SV[(size_t)bh * nsb + j * BC / 64];
+            lbias = __log2f(sv / svmax);
+            inv_r = svmax / sv;
+        }
+        const float ks = kscale(j);
+        bf16x8 pf[NQ][C::CH];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const float ct = cq[n] * ks;
+            const float bias = lbias - m_run[n];
+            float lsum = 0.f;
 #pragma unroll
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = kb + key8h + 32 * t + 16 * ((i >> 2) >> 1) + 4 * ((i >> 2) & 1) + (i & 3);
-                    if ((key >= N) || (CAUSAL && key > qrow)) s_cur[t][i] = -INFINITY;
+                    const float p = fast_exp2(__builtin_fmaf(s_cur[t][n][i], ct, bias));
+                    lsum += p;
+                    pf[n][2 * t + i / 8][i % 8] = (bf16_t)p;
                 }
+            if constexpr (C::F8) lsum *= inv_r;
+            l_run[n] += lsum;
         }
-        // ---- phase A: scores of block j+1 on the matrix cores, softmax of block j on the VALU
+        // ---- scores of block j+1
         if constexpr (PIPE && NEXT) qk(smK[B ^ 1], s_nxt);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < C::MT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[t][i]);
-        mx = pair_max(mx) * ct;
-        const float m_new = fmaxf(m_run, mx);
-        const bool grow = m_new > m_run + tau;
-        const float m_ref = grow ? m_new : m_run;
-        const float alpha = (grow && m_run != -INFINITY) ? fast_exp2(m_run - m_ref) : (grow ? 0.f : 1.f);
-        m_run = m_ref;
-        float bias = (m_run == -INFINITY) ? 0.f : -m_run;
-        float inv_r = 1.f;
-        if constexpr (C::F8) {
-            const float sv = SV[(size_t)bh * nsb + j];
-            bias += __log2f(sv / svmax);
-            inv_r = svmax / sv;
-        }
-        bf16x8 pf[C::CH];
-        float lsum = 0.f;
-#pragma unroll
-        for (int t = 0; t < C::MT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(__builtin_fmaf(s_cur[t][i], ct, bias));
-                lsum += p;
-                pf[2 * t + i / 8][i % 8] = (bf16_t)p;
-            }
-        if constexpr (C::F8) lsum *= inv_r;
-        l_run = l_run * alpha + lsum;
-        // ---- rescale the accumulator (rare with TAU > 0)
-        if (wave_any(grow)) {
-#pragma unroll
-            for (int e = 0; e < C::DT; ++e)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[e][i] *= alpha;
-        }
-        // ---- phase B: O^T += V_j^T P_j^T
+        // ---- O^T += V_j^T P_j^T
         const uint8_t* vt = smV[B];
 #pragma unroll
         for (int ch = 0; ch < C::CH; ++ch)
@@ -373,8 +457,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp + 4 * C::VROW_BYTES));
                 // concatenated as whole vectors (element-wise assembly is mis-compiled)
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], acc[e], 0, 0, 0);
+#pragma unroll
+                for (int n = 0; n < NQ; ++n)
+                    acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[n][ch], acc[n][e], 0, 0, 0);
             }
+        // ---- mask and row max of block j+1
+        if constexpr (PIPE && NEXT) {
+            if constexpr (MASKN) mask(s_nxt, kb + BC);
+            row_max(s_nxt, j + 1);
+        }
         if constexpr (C::F8) {
             if (NEXT) store_v(smV[B ^ 1]);
         }
@@ -382,7 +473,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         __syncthreads();
     };
 
-    // ---- prologue: K_0, V_0 (and K_1, S_0 with the pipeline)
+    // ---- prologue: K_0, V_0 (and K_1, the scores and row max of block 0 with the pipeline)
     load_k(0, smK[0]);
     load_v(0, smV[0]);
     if (PIPE && nkb > 1) load_k(BC, smK[1]);
@@ -391,49 +482,62 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     __syncthreads();
     if constexpr (PIPE) {
         qk(smK[0], s_buf[0]);
+        if (nfull == 0) mask(s_buf[0], 0);
+        row_max(s_buf[0], 0);
         __syncthreads();   // every wave is done with smK[0] before block 0 refills it
     }
 
+    // blocks in pairs (even j in buffer 0); block j+1's mask is needed iff j + 1 >= nfull
     int j = 0;
+    for (; j + 2 < nkb && j + 2 < nfull; j += 2) {
+        step(j, IC<0>{}, IC<1>{}, IC<0>{});
+        step(j + 1, IC<1>{}, IC<1>{}, IC<0>{});
+    }
     for (; j + 2 < nkb; j += 2) {
-        step(j, IC<0>{}, IC<1>{});
-        step(j + 1, IC<1>{}, IC<1>{});
+        if (j + 1 >= nfull) step(j, IC<0>{}, IC<1>{}, IC<1>{});
+        else step(j, IC<0>{}, IC<1>{}, IC<0>{});
+        step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
     }
     if (j + 1 < nkb) {
-        step(j, IC<0>{}, IC<1>{});
-        step(j + 1, IC<1>{}, IC<0>{});
+        if (j + 1 >= nfull) step(j, IC<0>{}, IC<1>{}, IC<1>{});
+        else step(j, IC<0>{}, IC<1>{}, IC<0>{});
+        step(j + 1, IC<1>{}, IC<0>{}, IC<0>{});
     } else {
-        step(j, IC<0>{}, IC<0>{});
+        step(j, IC<0>{}, IC<0>{}, IC<0>{});
     }
 
     // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2
-    const float l_tot = pair_sum(l_run);   // lanes l and l^32 hold the two halves of a row's sum
-    if (qrow < N) {
-        const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
-        bf16_t* op = O + head_off + (size_t)qrow * D + 4 * h;
 #pragma unroll
-        for (int e = 0; e < C::DT; ++e)
+    for (int n = 0; n < NQ; ++n) {
+        const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
+        if (qrow[n] < N) {
+            const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
+            bf16_t* op = O + head_off + (size_t)qrow[n] * D + 4 * h;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                bf16x4 ov;
+            for (int e = 0; e < C::DT; ++e)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[e][4 * a + b] * inv);
-                *(bf16x4*)(op + 32 * e + 8 * a) = ov;
-            }
-        if (LSE != nullptr && h == 0)
-            LSE[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+                for (int a = 0; a < 4; ++a) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[n][e][4 * a + b] * inv);
+                    *(bf16x4*)(op + 32 * e + 8 * a) = ov;
+                }
+            if (LSE != nullptr && h == 0)
+                LSE[(size_t)bh * N + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
+        }
     }
 }
 
-template <InKind KIND, int D, int BC, bool CAUSAL, int TAU, int MINB, bool PIPE = (D <= 128)>
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE>
 hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const float* sq, const float* sk,
                              const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream) {
-    const int numQB = (N + kBR - 1) / kBR;
+    constexpr int BR = 4 * 32 * NQ;
+    const int numQB = (N + BR - 1) / BR;
     const int nsb = (N + 63) / 64;
     const long long total = (long long)BH * numQB;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, CAUSAL, TAU, MINB, PIPE>), dim3((unsigned)total), dim3(kThreads), 0,
-                       stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e);
+    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE>), dim3((unsigned)total), dim3(kThreads),
+                       0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e);
     return hipGetLastError();
 }
 
