@@ -16,9 +16,11 @@ causal), the same count for every backend. Also reported:
   kernel sources changed since those counters were taken;
 - ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
   same workload on the host cores (a reported baseline, not the target);
-- ``extra``: the causal headline, the other workloads (including the FP8 path:
-  rotation/quantisation of Q, K, V plus the FP8 forward) and the FP8
-  quantiser's HBM throughput.
+- ``extra``: per-launch min/median/max of the headline; the causal headline, the
+  other workloads (including the FP8 path: rotation/quantisation of Q, K, V plus
+  the FP8 forward) and the FP8 quantiser's HBM throughput; the tiny fp32 case and
+  the short-sequence sweep in GB/s of algorithmic bytes, warm and with the
+  last-level cache flushed.
 
 ``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
 rocprofv3 byte counters); ``--only-headline`` skips the extra workloads.
@@ -87,8 +89,22 @@ def progress(msg: str) -> None:
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
-def time_launches(torch, fn, steps: int, warmup: int) -> float:
-    """Average milliseconds per call of fn (which launches on the current stream)."""
+def ramp(torch, fn, ms: float = 100.0) -> None:
+    """Untimed calls of fn for about `ms` of GPU time, so the clock has risen from idle."""
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5) * 1e3
+    for _ in range(int(ms / one)):
+        fn()
+    torch.cuda.synchronize()
+
+
+def time_launches(torch, fn, steps: int, warmup: int, ramp_ms: float = 0.0) -> float:
+    """Average milliseconds per call of fn (which launches on the current stream), after
+    `warmup` untimed calls (and, for the secondary workloads, ~ramp_ms of untimed calls)."""
+    if ramp_ms > 0:
+        ramp(torch, fn, ramp_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -100,6 +116,24 @@ def time_launches(torch, fn, steps: int, warmup: int) -> float:
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
+
+
+def launch_stats(torch, fn, n: int = 20, flush=None):
+    """Per-launch milliseconds (min, median, max) over n launches, each bracketed by its own
+    events on the current stream; flush() (untimed) runs before each launch if given."""
+    times = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    return {"min": round(times[0], 4), "median": round(times[len(times) // 2], 4), "max": round(times[-1], 4)}
 
 
 def calib_copy(torch):
@@ -160,11 +194,11 @@ def main():
     from exact_attention_06_amd import fa_fwd, fa_fwd_fp8, fa_prep_fp8
     from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_inputs, make_qkv
 
-    def bf16_case(w, causal, steps, warmup):
+    def bf16_case(w, causal, steps, warmup, ramp_ms=0.0):
         q, k, v = (x.cuda() for x in make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-        ms = time_launches(torch, lambda: fa_fwd(q, k, v, o, lse, causal=causal), steps, warmup)
+        ms = time_launches(torch, lambda: fa_fwd(q, k, v, o, lse, causal=causal), steps, warmup, ramp_ms)
         del q, k, v, o, lse
         return ms
 
@@ -174,6 +208,11 @@ def main():
     ms = bf16_case(w, False, args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
     progress(f"headline {ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    qh, kh, vh = (x.cuda() for x in make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype))
+    oh = torch.empty_like(qh)
+    lh = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    per_launch = launch_stats(torch, lambda: fa_fwd(qh, kh, vh, oh, lh), 20)
+    del qh, kh, vh, oh, lh
     traffic = read_traffic()
     result = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d) and % of MFMA peak, bf16 N=8k d=128",
@@ -193,15 +232,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
-    extra = {}
+    extra = {"headline_per_launch_ms": per_launch}
     if not args.only_headline:
         s2, w2 = max(5, args.steps // 2), 2
-        ms_c = bf16_case(w, True, args.steps, args.warmup)
+        ms_c = bf16_case(w, True, args.steps, args.warmup, 100.0)
         extra["headline_causal"] = {"ms": round(ms_c, 4), "TFLOP/s": round(w.flops(True) / ms_c / 1e9, 1)}
         for name, causal in [("b4h16n2k_d128", False), ("b4h16n2k_d128", True), ("long_n16k_d128", True),
                              ("b8h16n4k_d64", False), ("b8h16n4k_d256", False)]:
             wx = WORKLOADS[name]
-            m = bf16_case(wx, causal, s2, w2)
+            m = bf16_case(wx, causal, s2, w2, 100.0)
             extra[f"{name}{'_causal' if causal else ''}"] = {
                 "ms": round(m, 4), "TFLOP/s": round(wx.flops(causal) / m / 1e9, 1)}
             progress(f"{name} causal={causal}: {m:.3f} ms")
@@ -213,8 +252,8 @@ def main():
         v8, sv = fa_prep_fp8(v)
         o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device="cuda")
-        m_fwd = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), s2, w2)
-        m_prep = time_launches(torch, lambda: fa_prep_fp8(q, signs, q8, sq), s2, w2)
+        m_fwd = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), s2, w2, 100.0)
+        m_prep = time_launches(torch, lambda: fa_prep_fp8(q, signs, q8, sq), s2, w2, 100.0)
         prep_bytes = q.numel() * 5 + sq.numel() * 4
         extra["fp8_b4h16n8k_d128"] = {
             "fwd_ms": round(m_fwd, 4), "fwd_TFLOP/s": round(wf.flops(False) / m_fwd / 1e9, 1),
@@ -225,12 +264,34 @@ def main():
         }
         del q, k, v, q8, k8, v8, o, lse
         progress(f"fp8: fwd {m_fwd:.3f} ms, prep {m_prep:.3f} ms per tensor")
+        # tiny fp32 case (launch/latency bound) and short sequences (HBM bound): GB/s of the
+        # algorithmic bytes (Q, K, V read, O, LSE written), warm and with the 256 MB
+        # last-level cache flushed by a 512 MB write before each launch
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = lambda: scratch.fill_(1)
+        for name in ("tiny_f32", "short_b64h16n128_d128", "short_b64h16n256_d128", "short_b64h16n512_d128"):
+            wx = WORKLOADS[name]
+            q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
+            o = torch.empty_like(q)
+            lse = torch.empty((wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
+            nbytes = 4 * q.numel() * q.element_size() + lse.numel() * 4
+            fn = lambda: fa_fwd(q, k, v, o, lse)
+            ramp(torch, fn)
+            warm = launch_stats(torch, fn, 20)
+            cold = launch_stats(torch, fn, 20, flush)
+            extra[name] = {"bytes": nbytes, "warm_ms": warm, "cold_ms": cold,
+                           "warm_GB/s": round(nbytes / warm["median"] / 1e6, 1),
+                           "cold_GB/s": round(nbytes / cold["median"] / 1e6, 1),
+                           "TFLOP/s_warm": round(wx.flops(False) / warm["median"] / 1e9, 2)}
+            progress(f"{name}: warm {warm['median']:.4f} ms, cold {cold['median']:.4f} ms")
+            del q, k, v, o, lse
+        del scratch
         result["extra"] = extra
     # calibration GEMM (hipBLASLt via torch): what a plain bf16 GEMM sustains on this GPU now
     a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
     b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
     c = torch.empty_like(a)
-    g_ms = time_launches(torch, lambda: torch.mm(a, b, out=c), 10, 3)
+    g_ms = time_launches(torch, lambda: torch.mm(a, b, out=c), 10, 3, 100.0)
     gemm_tflops = 2.0 * 8192 ** 3 / g_ms / 1e9
     result["calibration_gemm"] = {"shape": "8192x8192x8192 bf16 torch.mm", "TFLOP/s": round(gemm_tflops, 1),
                                   "attention_frac_of_gemm": round(tflops / gemm_tflops, 4)}

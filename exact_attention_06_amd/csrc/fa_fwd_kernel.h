@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float p = fast_exp2(__builtin_fmaf(s_cur[t][n][i], ct, bias));
-                    lsum += p;
+                    lsum += p;   // fp32 P: the logsumexp needs the unrounded sum
                     pf[n][2 * t + i / 8][i % 8] = (bf16_t)p;
                 }
             if constexpr (C::F8) lsum *= inv_r;

@@ -65,6 +65,9 @@ WORKLOADS = {
         Workload("b4h16n8k_d128", 4, 16, 8192, 128, "bf16", (False, True), 7,
                  "headline bf16 N=8k d=128 (same shape as the fp8 case)"),
     ]
+    # short sequences: many heads, N/2 FLOPs per byte, below the MFMA/HBM ridge
+    + [Workload(f"short_b64h16n{n}_d128", 64, 16, n, 128, "bf16", (False,), 8,
+                f"short-sequence sweep, N={n} (bound by HBM)") for n in (128, 256, 512)]
 }
 
 OUTLIER_FRACTION = 0.001

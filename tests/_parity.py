@@ -1,7 +1,9 @@
 """Shared helpers for the GPU parity tests: tolerances and sampled oracle comparisons.
 
 Tolerances (the contract for the floating-point outputs):
-- bf16 output O: |O_gpu - O_ref| <= 1e-2 + 2^-8 |O_ref| element-wise, and mean <= 1e-3.
+- bf16 output O: |O_gpu - O_ref| <= 1e-2 + 2^-8 |O_ref| element-wise, and mean <= 1e-3
+  (for stress inputs outside the workloads whose |O| is near 1, the mean bound adds the
+  mean of half an ulp, 2^-9 |O_ref|: there rounding O alone costs ~8e-4 on average).
   The 1e-2 is the contract; 2^-8 |O_ref| (one bf16 ulp of the reference value) is the
   floor of a bf16 result: rounding O itself to bf16 costs up to half an ulp, and the
   probability that multiplies the dominant value row is rounded to bf16 once before the
