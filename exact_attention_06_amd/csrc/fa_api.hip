@@ -21,9 +21,11 @@ int check_common(int B, int H, int N, int d, float scale, int causal) {
     if (!headdim_ok(d)) return FA_ERR_HEADDIM;
     if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
-    // element offsets are computed in 64-bit; the grid and per-head row counts must fit int32
+    // element offsets are computed in 64-bit; the grid and per-head row counts must fit int32,
+    // and the bytes of one head of fp32 data (buffer ranges and offsets inside a head) too
     const long long rows = (long long)B * H * (long long)N;
     if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -75,7 +77,7 @@ const char* fa_status_string(int status) {
         case FA_OK: return "ok";
         case FA_ERR_NULLPTR: return "a required pointer is NULL";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case FA_ERR_SHAPE: return "invalid shape (negative size or too many rows)";
+        case FA_ERR_SHAPE: return "invalid shape (negative size, too many rows, or N*d*4 >= 2^31)";
         case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64, 128 or 256)";
         case FA_ERR_DTYPE: return "unsupported dtype";
         case FA_ERR_SCALE: return "scale must be finite and > 0";

@@ -9,11 +9,19 @@
 // scales: the score tile is s_Q s_K (Q8 K8^T); P is converted to FP8 after the online
 // rescale).
 //
-// prep_fp8_kernel: one workgroup per 64-row block of one (batch, head). Each thread holds a
-// quarter of one row in registers; the fast Walsh-Hadamard transform runs its first
-// log2(d/4) butterfly stages inside the thread and the last two across the 4 threads of the
-// row (lane xor 1, 2). Then the signs and 1/sqrt(d) are applied, the block amax is reduced,
-// s = amax / 448 and the codes are e4m3(clamp(x / s, +-448)) with the hardware RNE convert.
+// prep_fp8_kernel: one workgroup per 64-row block of one (batch, head). The 4 threads of a
+// lane quad share one row: thread q holds the elements 16 k + 4 q + j (j < 4), so each load
+// instruction of a quad reads 64 contiguous bytes. The fast Walsh-Hadamard transform pairs
+// elements along one index bit per butterfly stage, in any order: the bits of j and k are
+// stages inside the thread, the two bits of q are stages across the quad (DPP quad
+// permutations, no LDS). Then one multiply by +-1/sqrt(d)
+// applies the signs and the normalisation, the block amax is reduced, s = amax / 448, and
+// the codes are e4m3(x / s) with the hardware RNE convert. x / s is the correctly rounded
+// fp32 quotient, computed from r = RN(1/s) as q0 = x r, q = q0 + (x - q0 s) r (two FMAs;
+// Markstein's correction gives RN(x / s) for normal operands) instead of a full division.
+// No clamp is needed for a normal s: |x| <= amax gives |x / s| <= 448 (1 + 2^-23), which the
+// convert rounds to 448; only a subnormal s (amax below ~5e-36) can exceed that, and such
+// blocks take a clamping branch. NaN inputs stay NaN.
 // Memory-bound: reads 4 bytes and writes 1 byte per element.
 //
 // The FP8 forward itself is the shared fused kernel (fa_fwd_kernel.h) instantiated for e4m3
@@ -33,29 +41,42 @@ constexpr float kE4m3Max = 448.f;
 // ------------------------------------------------------------------------------------------
 // rotation + quantisation
 // ------------------------------------------------------------------------------------------
+// value of lane l ^ 1 / l ^ 2 within each quad of lanes (DPP quad permutations; every lane
+// has a source, so the move can be folded into the instruction that uses it)
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
                                                             float* __restrict__ S, const float* __restrict__ signs,
                                                             int N, int nsb, float inv_sqrt_d) {
-    constexpr int NV = D / 4;   // values per thread
+    constexpr int NV = D / 4;   // values per thread: x[4 k + j] is element 16 k + 4 qd + j
     __shared__ float wmax[kPrepThreads / kWave];
     const int tid = threadIdx.x;
     const int blk = blockIdx.x;            // (bh, sb) flattened
     const int bh = blk / nsb;
     const int sb = blk - bh * nsb;
     const int row = sb * kRowsPerScale + (tid >> 2);
-    const int qd = tid & 3;
+    const int qd = tid & 3;                // quarter of the row; the 4 quarters are one lane quad
     const bool ok = row < N;
-    const size_t base = ((size_t)bh * N + (ok ? row : 0)) * D + qd * NV;
+    const size_t base = ((size_t)bh * N + (ok ? row : 0)) * D + 4 * qd;   // element 16 k + 4 qd + j
 
+    // rows past N (ragged last block) read as zero through the buffer's range check
+    const __amdgpu_buffer_rsrc_t rX =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)bh * N * D), (short)0, N * D * 4, kBufferConfig);
+    const int off = (row * D + 4 * qd) * 4;
     float x[NV];
 #pragma unroll
     for (int i = 0; i < NV; i += 4) {
-        f32x4 v = ok ? *(const f32x4*)(X + base + i) : f32x4{};
+        const f32x4 v = __builtin_bit_cast(f32x4, buffer_load16(rX, off + 16 * i));
         x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
     }
     if (signs != nullptr) {
-        // in-thread butterflies: strides 1 .. NV/2
+        // in-thread butterflies: register strides 1 .. NV/2 (element bits 0, 1 and 4 ..)
 #pragma unroll
         for (int st = 1; st < NV; st <<= 1)
 #pragma unroll
@@ -65,18 +86,22 @@ __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __r
                     x[i] = a + b;
                     x[i + st] = a - b;
                 }
-        // cross-thread butterflies: strides NV and 2 NV (partner lane xor 1, xor 2)
+        // cross-thread butterflies: element bits 2 and 3 (lane xor 1, xor 2); the lower
+        // partner keeps x + y, the upper one y - x, i.e. (+-x) + y
+        const float sg1 = (qd & 1) ? -1.f : 1.f;
+        const float sg2 = (qd & 2) ? -1.f : 1.f;
+        // (x * +-1 is exact; a separate add, not an FMA, takes the DPP operand)
 #pragma unroll
-        for (int m = 1; m <= 2; m <<= 1) {
-            const bool upper = (qd & m) != 0;
+        for (int i = 0; i < NV; ++i) x[i] = __fadd_rn(quad_xor1(x[i]), __fmul_rn(x[i], sg1));
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const float other = __shfl_xor(x[i], m);
-                x[i] = upper ? (other - x[i]) : (x[i] + other);
-            }
+        for (int i = 0; i < NV; ++i) x[i] = __fadd_rn(quad_xor2(x[i]), __fmul_rn(x[i], sg2));
+        // signs and 1/sqrt(d) in one multiply: x (+-c) = +-(x c), the same bits as (x c) (+-1)
+#pragma unroll
+        for (int i = 0; i < NV; i += 4) {
+            const f32x4 sv = *(const f32x4*)(signs + 4 * i + 4 * qd);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[i + u] *= sv[u] * inv_sqrt_d;
         }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) x[i] = (x[i] * inv_sqrt_d) * signs[qd * NV + i];
     }
     // block amax
     float am = 0.f;
@@ -88,26 +113,27 @@ __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __r
     __syncthreads();
     am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = (am == 0.f) ? 1.f : __fdiv_rn(am, kE4m3Max);
+    const float r = __fdiv_rn(1.f, s);     // RN(1/s)
+    const bool tiny = s < 1.17549435e-38f; // subnormal scale: quotients may exceed 448
     if (tid == 0) S[(size_t)bh * nsb + sb] = s;
     if (!ok) return;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const float q0 = __fmul_rn(x[i], r);
+        x[i] = __builtin_fmaf(__builtin_fmaf(-q0, s, x[i]), r, q0);   // RN(x / s)
+    }
+    if (tiny) {   // uniform per block, rare
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            x[i] = x[i] > kE4m3Max ? kE4m3Max : (x[i] < -kE4m3Max ? -kE4m3Max : x[i]);   // keeps NaN
+    }
     uint8_t* out = X8 + base;
 #pragma unroll
-    for (int i = 0; i < NV; i += 16) {
-        i32x4 pk;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            float y[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float t = __fdiv_rn(x[i + 4 * w + u], s);
-                t = t > kE4m3Max ? kE4m3Max : (t < -kE4m3Max ? -kE4m3Max : t);   // saturate, keep NaN
-                y[u] = t;
-            }
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
-            pk[w] = word;
-        }
-        *(i32x4*)(out + i) = pk;
+    for (int i = 0; i < NV; i += 4) {
+        const float* y = x + i;
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+        *(int*)(out + 4 * i) = word;
     }
 }
 

@@ -50,7 +50,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULLPTR = -1,   /* a required pointer is NULL */
     FA_ERR_ALIGN = -2,     /* a pointer is not 16-byte aligned */
-    FA_ERR_SHAPE = -3,     /* B, H or N negative, or B*H*N*d does not fit the index range */
+    FA_ERR_SHAPE = -3,     /* B, H or N negative, B*H*N > 2^31 - 1, or N*d*4 > 2^31 - 1 (one
+                              head's fp32 bytes must fit the 31-bit range of buffer offsets) */
     FA_ERR_HEADDIM = -4,   /* d is not 64, 128 or 256 */
     FA_ERR_DTYPE = -5,     /* dtype is not one of fa_dtype */
     FA_ERR_SCALE = -6,     /* scale is not finite and > 0 */

@@ -67,6 +67,8 @@ def test_fwd_argument_errors(L):
     assert fwd(L, B=-1) == -3
     assert fwd(L, N=-5) == -3
     assert fwd(L, B=1 << 16, H=1 << 16, N=1) == -3     # B*H*N beyond the int32 row range
+    assert fwd(L, N=1 << 21, d=256) == -3               # one head's fp32 bytes reach 2^31
+    assert L.fa_prep_fp8(P, P, P, None, 1, 1, 1 << 21, 256, None) == -3
     assert fwd(L, q=None) == -1
     assert fwd(L, o=None) == -1
     assert fwd(L, k=P + 8) == -2
