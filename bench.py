@@ -57,14 +57,18 @@ def parse_args():
     return p.parse_args()
 
 
+# the sources the headline kernel (bf16 forward) is compiled from
+HEADLINE_SOURCES = ("fa_common.h", "fa_fwd_kernel.h", "fa_fwd_bf16.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counter readings are still current."""
+    """Hash of the headline kernel's sources, to tell whether stored counter readings of that
+    kernel are still current."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in HEADLINE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
