@@ -506,25 +506,54 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         step(j, IC<0>{}, IC<0>{}, IC<0>{});
     }
 
-    // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2
+    // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2. Each wave stages its 32 x d bf16
+    // tile of O in LDS (the tile slots are free after the last barrier) and writes it back in
+    // whole rows, 16 bytes per lane: a lane's own results are 4-element runs scattered over
+    // the d range, which would make every store instruction touch 32 rows.
+    constexpr int OROW = D * 2;                        // bytes per bf16 row of O
+    constexpr int OSTAGE = 32 * OROW;                  // one wave's tile
+    constexpr int OSW = (OROW / 16 < 16 ? OROW / 16 : 16) - 1;   // XOR mask of the 16-byte chunks
+    constexpr bool KFITS = C::K_BYTES >= OSTAGE;       // V slots always fit (BC >= 32 rows)
+    static_assert(C::V_BYTES >= OSTAGE, "a V slot must hold a wave's O tile");
+    constexpr int LPR = OROW / 16;                     // lanes per row in the write-back
+    constexpr int RPI = kWave / LPR;                   // rows per write-back instruction
+    uint8_t* const stg = (wave & 1) ? ((KFITS && wave >= 2) ? smK1 : smV1) : ((KFITS && wave >= 2) ? smK0 : smV0);
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
-        if (qrow[n] < N) {
-            const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
-            bf16_t* op = O + head_off + (size_t)qrow[n] * D + 4 * h;
+    for (int round = 0; round < (KFITS ? 1 : 2); ++round) {
+        if (KFITS || (wave >> 1) == round) {
 #pragma unroll
-            for (int e = 0; e < C::DT; ++e)
+            for (int n = 0; n < NQ; ++n) {
+                const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
+                const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
+                // result register 4a + b of d tile e holds d = 32 e + 8 a + 4 h + b of query col:
+                // 16-byte chunk 4 e + a of the row, half h
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    bf16x4 ov;
+                for (int e = 0; e < C::DT; ++e)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[n][e][4 * a + b] * inv);
-                    *(bf16x4*)(op + 32 * e + 8 * a) = ov;
+                    for (int a = 0; a < 4; ++a) {
+                        bf16x4 ov;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[n][e][4 * a + b] * inv);
+                        *(bf16x4*)(stg + col * OROW + 16 * ((4 * e + a) ^ (col & OSW)) + 8 * h) = ov;
+                    }
+                if (LSE != nullptr && h == 0 && qrow[n] < N)
+                    LSE[(size_t)bh * N + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                // the wave reads back what its other lanes wrote
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+                __builtin_amdgcn_wave_barrier();
+                const int qt0 = q0w + 32 * n;
+#pragma unroll
+                for (int it = 0; it < 32 / RPI; ++it) {
+                    const int r = RPI * it + lane / LPR;
+                    const int c = lane % LPR;
+                    const i32x4 v = *(const i32x4*)(stg + r * OROW + 16 * (c ^ (r & OSW)));
+                    if (qt0 + r < N) *(i32x4*)((uint8_t*)(O + head_off + (size_t)(qt0 + r) * D) + 16 * c) = v;
                 }
-            if (LSE != nullptr && h == 0)
-                LSE[(size_t)bh * N + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+            }
         }
+        if (!KFITS && round == 0) __syncthreads();
     }
 }
 
