@@ -54,11 +54,10 @@ namespace fa {
 
 enum class InKind { BF16, FP8 };
 
-constexpr int kThreads = 256;   // 4 waves
 // buffer resource word 3 for raw (untyped) 32-bit-offset buffer loads on gfx950
 constexpr int kBufferConfig = 0x00020000;
 
-template <InKind KIND, int D, int BC>
+template <InKind KIND, int D, int BC, int NT>
 struct FwdCfg {
     static constexpr bool F8 = KIND == InKind::FP8;
     static constexpr int IN_BYTES = F8 ? 1 : 2;            // bytes per element in HBM
@@ -73,9 +72,9 @@ struct FwdCfg {
     static constexpr int CH = BC / 16;                      // 16-key chunks of the PV product
     static constexpr int K_BYTES = BC * ROW_BYTES;
     static constexpr int V_BYTES = BC * VROW_BYTES;
-    static constexpr int K_LOADS = K_BYTES / 16 / kThreads;            // direct loads per thread
-    static constexpr int V_LOADS = F8 ? BC * D / 16 / kThreads : V_BYTES / 16 / kThreads;
-    static_assert(K_LOADS >= 1 && K_LOADS * kThreads * 16 == K_BYTES, "K tile must split evenly");
+    static constexpr int K_LOADS = K_BYTES / 16 / NT;            // direct loads per thread
+    static constexpr int V_LOADS = F8 ? BC * D / 16 / NT : V_BYTES / 16 / NT;
+    static_assert(K_LOADS >= 1 && K_LOADS * NT * 16 == K_BYTES, "K tile must split evenly");
     static_assert(V_LOADS >= 1, "V tile must split evenly");
     // FP8: a key block lies inside one 64-row scale block of K and V
     static_assert(!F8 || 64 % BC == 0, "FP8 key blocks must divide the 64-row scale blocks");
@@ -99,19 +98,21 @@ struct QOperand<InKind::FP8> { typedef i32x8 type; };
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// NQ: 32-query tiles per wave (the workgroup owns 4 * 32 * NQ queries). With NQ = 2 every K
+// WAVES: waves per workgroup (each owns 32 NQ queries; all share the K/V tiles).
+// NQ: 32-query tiles per wave (the workgroup owns WAVES * 32 * NQ queries). With NQ = 2 every K
 // and V^T operand read from LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
 // PIPE: compute the scores of block j+1 while the softmax of block j runs (needs registers
 // for two score tiles); without it each block's scores are computed just before its softmax.
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE>
-__global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
     bf16_t* __restrict__ O, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */) {
-    using C = FwdCfg<KIND, D, BC>;
+    constexpr int NT = 64 * WAVES;    // threads per workgroup
+    using C = FwdCfg<KIND, D, BC, NT>;
     using QT = typename QOperand<KIND>::type;
     constexpr float tau = (float)TAU;
-    constexpr int BR = 4 * 32 * NQ;   // queries per workgroup
+    constexpr int BR = WAVES * 32 * NQ;   // queries per workgroup
     // separate objects per buffer, so that the compiler can tell that LDS reads of one
     // buffer do not depend on the DMA writes still in flight into the other one
     __shared__ __attribute__((aligned(1024))) uint8_t smK0[C::K_BYTES];
@@ -196,15 +197,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     // a multiple of the swizzle period (16 rows for K, 4 for V) every load of the thread has
     // the same swizzle, and its offsets are one register plus constants (fewer live VGPRs).
     constexpr int KRPL = 1024 / C::ROW_BYTES;
-    constexpr bool KUNI = (4 * KRPL) % 16 == 0;
+    constexpr bool KUNI = (WAVES * KRPL) % 16 == 0;
     constexpr int KN = KUNI ? 1 : C::K_LOADS;
     int koff[KN];
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
-        const int r = KRPL * (wave + 4 * i) + lane / C::KCPR;
+        const int r = KRPL * (wave + WAVES * i) + lane / C::KCPR;
         koff[i] = r * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(r, lane % C::KCPR);
     }
-    auto koff_of = [&](int i) { return KUNI ? koff[0] + 4 * KRPL * C::ROW_BYTES * i : koff[i]; };
+    auto koff_of = [&](int i) { return KUNI ? koff[0] + WAVES * KRPL * C::ROW_BYTES * i : koff[i]; };
     constexpr int VRPL = 1024 / C::VROW_BYTES;
     int voff0;
     if constexpr (C::F8) {
@@ -217,13 +218,13 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         voff0 = r * C::ROW_BYTES + 16 * v_slot<C::VSWZ>(r, lane % C::VCPR);
     }
     auto voff_of = [&](int i) {
-        if constexpr (C::F8) return voff0 + (kThreads / (D / 16)) * C::ROW_BYTES * i;
-        return voff0 + 4 * VRPL * C::ROW_BYTES * i;   // rows 4 VRPL apart keep the V swizzle
+        if constexpr (C::F8) return voff0 + (NT / (D / 16)) * C::ROW_BYTES * i;
+        return voff0 + WAVES * VRPL * C::ROW_BYTES * i;   // rows WAVES VRPL apart keep the V swizzle
     };
     auto load_k = [&](int kb, uint8_t* dst) {
 #pragma unroll
         for (int i = 0; i < C::K_LOADS; ++i)
-            lds_dma16(rK, dst + 1024 * (wave + 4 * i), koff_of(i) + kb * C::ROW_BYTES);
+            lds_dma16(rK, dst + 1024 * (wave + WAVES * i), koff_of(i) + kb * C::ROW_BYTES);
     };
     i32x4 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
     auto load_v = [&](int kb, uint8_t* dst) {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
             if constexpr (C::F8)
                 vst[i] = buffer_load16(rV, voff_of(i) + kb * C::ROW_BYTES);
             else
-                lds_dma16(rV, dst + 1024 * (wave + 4 * i), voff_of(i) + kb * C::ROW_BYTES);
+                lds_dma16(rV, dst + 1024 * (wave + WAVES * i), voff_of(i) + kb * C::ROW_BYTES);
         }
     };
     // FP8: expand the staged e4m3 V chunks exactly to bf16 and store them swizzled
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
         if constexpr (C::F8) {
 #pragma unroll
             for (int i = 0; i < C::V_LOADS; ++i) {
-                const int x = tid + kThreads * i;
+                const int x = tid + NT * i;
                 const int r = x / (D / 16);
                 const int c8 = x % (D / 16);   // 16 e4m3 values = bf16 chunks 2 c8 and 2 c8 + 1
                 i32x4 lo, hi;
@@ -517,10 +518,15 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
     static_assert(C::V_BYTES >= OSTAGE, "a V slot must hold a wave's O tile");
     constexpr int LPR = OROW / 16;                     // lanes per row in the write-back
     constexpr int RPI = kWave / LPR;                   // rows per write-back instruction
-    uint8_t* const stg = (wave & 1) ? ((KFITS && wave >= 2) ? smK1 : smV1) : ((KFITS && wave >= 2) ? smK0 : smV0);
+    // staging slots: the V tiles, and the K tiles when they are large enough; waves take
+    // turns when there are fewer slots than waves
+    constexpr int NSLOT = KFITS ? 4 : 2;
+    constexpr int ROUNDS = (WAVES + NSLOT - 1) / NSLOT;
+    const int slot = wave % NSLOT;
+    uint8_t* const stg = slot == 0 ? smV0 : slot == 1 ? smV1 : slot == 2 ? smK0 : smK1;
 #pragma unroll
-    for (int round = 0; round < (KFITS ? 1 : 2); ++round) {
-        if (KFITS || (wave >> 1) == round) {
+    for (int round = 0; round < ROUNDS; ++round) {
+        if (wave / NSLOT == round) {
 #pragma unroll
             for (int n = 0; n < NQ; ++n) {
                 const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
@@ -553,19 +559,19 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_kernel(
                 __builtin_amdgcn_wave_barrier();
             }
         }
-        if (!KFITS && round == 0) __syncthreads();
+        if (round + 1 < ROUNDS) __syncthreads();
     }
 }
 
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE>
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES = 4>
 hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const float* sq, const float* sk,
                              const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream) {
-    constexpr int BR = 4 * 32 * NQ;
+    constexpr int BR = WAVES * 32 * NQ;
     const int numQB = (N + BR - 1) / BR;
     const int nsb = (N + 63) / 64;
     const long long total = (long long)BH * numQB;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE>), dim3((unsigned)total), dim3(kThreads),
+    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES>), dim3((unsigned)total), dim3(64 * WAVES),
                        0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e);
     return hipGetLastError();
 }

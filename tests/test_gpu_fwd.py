@@ -54,6 +54,8 @@ def check_full(q, k, v, causal, dtype, scale=None, mean_floor=False):
 SMALL = [  # (B, H, N, d): several 128-query / 64-key tiles, ragged tails, edge lengths
     (2, 3, 300, 64), (2, 3, 300, 128), (1, 2, 200, 256), (1, 1, 1, 128), (1, 1, 63, 64),
     (1, 2, 129, 128), (1, 1, 64, 256), (1, 1, 65, 256), (3, 1, 257, 128), (1, 2, 1000, 64),
+    # d = 128 at N >= 2048 takes the 256-query (8-wave) workgroups when non-causal
+    (1, 1, 2048, 128), (1, 2, 2100, 128),
 ]
 
 
