@@ -1,4 +1,4 @@
-"""CPU oracle for the exact-attention forward pass (test infrastructure only).
+"""CPU oracle for exact attention, forward and backward (test infrastructure only).
 
 This package is the reference that the GPU path is checked against. It is plain,
 slow and meant to be read against the pages line by line: float64 NumPy, the
@@ -20,6 +20,9 @@ hadamard   the normalised Sylvester Hadamard matrix and the random-sign
            incoherent rotation x -> x H D.
 fp8        per-64-row block quantisation and the two FP8 reference results
            (O_true on the original inputs, O_deq on the dequantised ones).
+attention_bwd
+           the closed-form gradients dQ, dK, dV (P rebuilt from L, D = rowsum(dO o O),
+           dS = P o (dP - D)), materialised for short rows or sampled for long ones.
 """
 
 from .attention import (  # noqa: F401
