@@ -16,7 +16,8 @@ causal), the same count for every backend. Also reported:
   kernel sources changed since those counters were taken;
 - ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
   same workload on the host cores (a reported baseline, not the target);
-- ``extra``: per-launch min/median/max of the headline; the causal headline, the
+- ``extra``: per-launch min/median/max of the headline; the backward (dQ, dK, dV;
+  FLOPs counted as 2.5x the forward's, the five products of the backward); the causal headline, the
   other workloads (including the FP8 path: rotation/quantisation of Q, K, V plus
   the FP8 forward) and the FP8 quantiser's HBM throughput; the tiny fp32 case and
   the short-sequence sweep in GB/s of algorithmic bytes, warm and with the
@@ -248,6 +249,22 @@ def main():
             extra[f"{name}{'_causal' if causal else ''}"] = {
                 "ms": round(m, 4), "TFLOP/s": round(wx.flops(causal) / m / 1e9, 1)}
             progress(f"{name} causal={causal}: {m:.3f} ms")
+        # backward (dQ, dK, dV): FLOPs counted as the page's five products, 2.5x the forward
+        from exact_attention_06_amd import fa_bwd
+        from exact_attention_06_amd.workloads import make_dout
+        for name, causal in [("b4h16n8k_d128", False), ("b4h16n8k_d128", True), ("b4h16n2k_d128", False),
+                             ("b8h16n4k_d64", False)]:
+            wx = WORKLOADS[name]
+            q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
+            do = make_dout(wx.B, wx.H, wx.N, wx.d, wx.seed).cuda()
+            o, lse = fa_fwd(q, k, v, causal=causal)
+            dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+            delta = torch.empty((wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
+            m = time_launches(torch, lambda: fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal), s2, w2, 100.0)
+            extra[f"bwd_{name}{'_causal' if causal else ''}"] = {
+                "ms": round(m, 4), "TFLOP/s": round(2.5 * wx.flops(causal) / m / 1e9, 1)}
+            progress(f"bwd {name} causal={causal}: {m:.3f} ms")
+            del q, k, v, do, o, lse, dq, dk, dv, delta
         # FP8 path: prep of Q, K (rotated) and V, then the FP8 forward
         wf = WORKLOADS["fp8_b4h16n8k_d128"]
         q, k, v, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))

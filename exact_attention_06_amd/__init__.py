@@ -1,4 +1,4 @@
-"""Exact (Flash) attention forward pass for AMD Instinct MI355X (gfx950).
+"""Exact (Flash) attention, forward and backward, for AMD Instinct MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind the C ABI of
 ``libfa.so`` (include/fa.h); this package is its Python binding:
@@ -7,11 +7,12 @@ The computation runs in hand-written HIP kernels behind the C ABI of
   float32 or bfloat16 [B, H, N, d] tensors, returning O and the row logsumexp;
 - ``fa_prep_fp8(x, signs)``: random-Hadamard rotation and per-64-row E4M3
   block quantisation of a float32 tensor;
-- ``fa_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)``: attention forward on E4M3 codes.
+- ``fa_fwd_fp8(q8, k8, v8, sq, sk, sv, ...)``: attention forward on E4M3 codes;
+- ``fa_bwd(q, k, v, o, dout, lse, ...)``: the gradients dq, dk, dv (bfloat16).
 
 ``workloads`` draws the seeded synthetic inputs; ``build`` compiles the library.
 """
 
-from ._lib import FAError, fa_fwd, fa_fwd_fp8, fa_prep_fp8, lib, status_string  # noqa: F401
+from ._lib import FAError, fa_bwd, fa_fwd, fa_fwd_fp8, fa_prep_fp8, lib, status_string  # noqa: F401
 
-__all__ = ["FAError", "fa_fwd", "fa_fwd_fp8", "fa_prep_fp8", "lib", "status_string"]
+__all__ = ["FAError", "fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_prep_fp8", "lib", "status_string"]

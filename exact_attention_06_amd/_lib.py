@@ -23,7 +23,7 @@ STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_ALIGN", -3: "FA_ERR_SHAPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.fa_prep_fp8.restype = i
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     L.fa_fwd_fp8.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    L.fa_bwd.restype = i
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -159,3 +161,26 @@ def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=F
     _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv), _ptr(o), _ptr(lse),
                             B, H, N, d, scale, int(bool(causal)), _stream(stream)))
     return o, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scale=None, causal=False, stream=None):
+    """Gradients (dq, dk, dv) of attention from the forward's inputs, output o, logsumexp
+    lse and the output gradient dout; bfloat16 [B, H, N, d] tensors, lse float32 [B, H, N].
+    Outputs and the fp32 [B, H, N] workspace ``delta`` are allocated here unless given."""
+    B, H, N, d = _bhnd(q)
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v, o, dout must be bfloat16 [B, H, N, d] tensors of one shape")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward takes bfloat16 tensors")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    _require_gpu(q, k, v, o, dout, lse, dq, dk, dv, delta)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(delta), B, H, N, d, scale, int(bool(causal)), FA_BF16, _stream(stream)))
+    return dq, dk, dv

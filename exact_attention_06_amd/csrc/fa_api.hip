@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;   // 0.1.0
+constexpr int kVersion = 200;   // 0.2.0: fa_bwd
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -72,13 +72,29 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq, 
                                        static_cast<hipStream_t>(stream)));
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* stream) {
+    int st = check_common(B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta))
+        return FA_ERR_ALIGN;
+    return from_hip(fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B * H, N, d, scale, causal != 0,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULLPTR: return "a required pointer is NULL";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case FA_ERR_SHAPE: return "invalid shape (negative size, too many rows, or N*d*4 >= 2^31)";
-        case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64, 128 or 256)";
+        case FA_ERR_HEADDIM: return "unsupported head dimension (64, 128 or 256; the backward: 64 or 128)";
         case FA_ERR_DTYPE: return "unsupported dtype";
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -1,0 +1,455 @@
+// bf16 attention backward: dQ, dK, dV from Q, K, V, O, dO and the forward's logsumexp.
+//
+// Source: "FlashAttention 2 & 3: Work Partitioning, Warp Specialization & FP8", section
+// "The backward pass: recompute, and the one identity that makes it tile-able": the
+// probabilities are rebuilt from the saved logsumexp, P = exp(S - L); dV = P^T dO,
+// dP = dO V^T, D = rowsum(dO o O), dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+// The same page (section "Edit 3" and the backward section) parallelises the backward over
+// key blocks so that dK and dV accumulate locally, and names fp32 atomics or a separate pass
+// for dQ; this file takes the separate pass (deterministic, no atomics):
+//
+// 1. bwd_delta_kernel: D = rowsum(dO o O) in fp32, one row per group of d/8 lanes.
+// 2. bwd_dq_kernel, parallel over 128-query blocks (the forward's layout): each wave keeps
+//    Q^T and dO^T of its 32 queries in registers as MFMA B operands and streams 32-key blocks
+//    of K and V through LDS. S^T = K Q^T and dP^T = V dO^T put one query in each lane pair;
+//    P^T = exp2(S^T c - L log2 e) and dS^T = P^T o (dP^T - D) stay in registers and are the B
+//    operand (bf16) of dQ^T += K^T dS^T, whose A operand K^T comes from the LDS transpose read.
+// 3. bwd_dkdv_kernel, parallel over 128-key blocks: each wave keeps K^T and V^T of its 32 keys
+//    in registers and streams 32-query blocks of Q and dO through LDS. S = Q K^T and
+//    dP = dO V^T put one key in each lane pair; P and dS (bf16) are the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T from the LDS transpose read.
+//
+// MFMA layouts as in fa_common.h. The rows of the A operand of S / S^T are fed in the order
+// swap_bits23, so that result registers 8u .. 8u+7 of lane half h hold rows 16u + 8h + 0..7:
+// exactly the B operand of a 32x32x16 product over those 16 rows. Tiles are row-major bf16 in
+// LDS, loaded straight from HBM (buffer_load ... lds; rows past N read as zero), 16-byte
+// chunks XOR-swizzled by swap_bits23(row) like the forward's K tiles.
+#include "fa_common.h"
+#include "fa_fwd_kernel.h"   // k_slot, kBufferConfig
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdThreads = 256;   // 4 waves
+constexpr int kBwdRows = 32;       // rows per streamed tile (keys in dq, queries in dkdv)
+
+// ------------------------------------------------------------------------------------------
+// D = rowsum(dO o O)
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __restrict__ O,
+                                                                const bf16_t* __restrict__ dO,
+                                                                float* __restrict__ delta, long long rows) {
+    constexpr int LPR = D / 8;           // lanes per row, 8 bf16 each
+    constexpr int RPW = kWave / LPR;     // rows per wave
+    const int lane = threadIdx.x & 63;
+    const long long row = ((long long)blockIdx.x * (kBwdThreads / kWave) + (threadIdx.x >> 6)) * RPW + lane / LPR;
+    const int c = lane % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const bf16x8 a = *(const bf16x8*)(O + row * D + 8 * c);
+        const bf16x8 b = *(const bf16x8*)(dO + row * D + 8 * c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = __builtin_fmaf((float)a[j], (float)b[j], acc);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (c == 0 && row < rows) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// shared pieces of the two MFMA kernels
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct BwdCfg {
+    static constexpr int ROW = D * 2;                    // bytes per bf16 row
+    static constexpr int CPR = ROW / 16;                 // 16-byte chunks per row
+    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+    static constexpr int KSTEPS = D / 16;                // 32x32x16 products over d
+    static constexpr int DT = D / 32;                    // 32-wide d tiles of a transposed accumulator
+    static constexpr int TB = kBwdRows * ROW;            // bytes of one streamed tile
+    static constexpr int RPL = 1024 / ROW;               // rows per 1 KB DMA region
+    static constexpr int LOADS = TB / 1024 / 4;          // DMA loads per thread per tile
+    static_assert(LOADS >= 1, "tile must give every thread a load");
+    static constexpr int KSPAN = 8;                      // steps per 16 chunks
+    static constexpr int KA = KSTEPS < KSPAN ? KSTEPS : KSPAN;
+    static constexpr int EA = DT < 4 ? DT : 4;           // 4 d tiles = 16 chunks
+};
+
+// Per-lane addresses inside a swizzled 32-row tile:
+// - rd[s]: A-operand row reads, row swap_bits23(col), chunk 2s + h (steps s and s+8 are 256
+//   bytes apart);
+// - trlo[e] / trhi[e]: transposed reads of d tile e for the 16-row chunk 0 (rows 16 apart keep
+//   the swizzle): lane (g, L) reads 8 bytes of row 8(g>>1) + (L>>2) (and the row 4 below),
+//   columns 32e + 16(g&1) + 4(L&3) .. +3, as ds_read_b64_tr_b16 expects.
+// - dma[i]: source offsets of the tile loads (load i of wave w fills 1 KB region w + 4i).
+template <int D>
+struct TileAddr {
+    using C = BwdCfg<D>;
+    int rd[C::KA];
+    int trlo[C::EA], trhi[C::EA];
+    int dma[C::LOADS];
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int h = lane >> 5, col = lane & 31;
+        const int rr = swap_bits23(col);
+#pragma unroll
+        for (int s = 0; s < C::KA; ++s) rd[s] = rr * C::ROW + 16 * k_slot<C::SWZ>(rr, 2 * s + h);
+        const int g = lane >> 4, L = lane & 15;
+        const int r0 = 8 * (g >> 1) + (L >> 2);
+#pragma unroll
+        for (int e = 0; e < C::EA; ++e) {
+            const int byte = 64 * e + 32 * (g & 1) + 8 * (L & 3);
+            trlo[e] = r0 * C::ROW + 16 * k_slot<C::SWZ>(r0, byte / 16) + (byte & 15);
+            trhi[e] = (r0 + 4) * C::ROW + 16 * k_slot<C::SWZ>(r0 + 4, byte / 16) + (byte & 15);
+        }
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int r = C::RPL * (wave + 4 * i) + lane / C::CPR;
+            dma[i] = r * C::ROW + 16 * k_slot<C::SWZ>(r, lane % C::CPR);
+        }
+    }
+    // 32 rows starting at row0 of the buffer r into tile dst
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int row0, int wave) const {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) lds_dma16(r, dst + 1024 * (wave + 4 * i), dma[i] + row0 * C::ROW);
+    }
+    // A operand (32 rows x 16 d) of step s
+    __device__ __forceinline__ bf16x8 row_operand(const uint8_t* t, int s) const {
+        return *(const bf16x8*)(t + 256 * (s / C::KSPAN) + rd[s % C::KSPAN]);
+    }
+    // A operand (32 d x 16 rows) of d tile e and 16-row chunk ch, from the transposed read
+    __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* t, int e, int ch) const {
+        const uint8_t* base = t + 16 * ch * C::ROW + 256 * (e / 4);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, base + trlo[e % 4]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, base + trhi[e % 4]));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);   // whole-vector concatenation
+    }
+};
+
+// B operand of a wave's 32 resident rows (query or key `row`): 16 values of d per step,
+// [16 s + 8 h, +8); zeros past N
+template <int D>
+__device__ __forceinline__ void load_resident(bf16x8 (&f)[D / 16], const bf16_t* base, int row, int N, int h) {
+    const bool ok = row < N;
+    const bf16_t* p = base + (size_t)(ok ? row : 0) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) f[s] = ok ? *(const bf16x8*)(p + 16 * s) : bf16x8{};
+}
+
+// Write a wave's transposed fp32 accumulator (lane = row col, register 4a+b of d tile e =
+// column 32e + 8a + 4h + b) as bf16 rows times `mult`, staged through the wave's LDS tile
+// `stg` (32 x d) so that the global stores are whole rows, 16 bytes per lane.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mult, uint8_t* stg, bf16_t* out,
+                                           int row0, int N, int lane) {
+    using C = BwdCfg<D>;
+    const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            bf16x4 ov;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[e][4 * a + b] * mult);
+            *(bf16x4*)(stg + col * C::ROW + 16 * ((4 * e + a) ^ (col & C::SWZ)) + 8 * h) = ov;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave reads back what its lanes wrote
+    __builtin_amdgcn_wave_barrier();
+    constexpr int LPR = C::ROW / 16, RPI = kWave / LPR;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = RPI * it + lane / LPR;
+        const int c = lane % LPR;
+        const i32x4 v = *(const i32x4*)(stg + r * C::ROW + 16 * (c ^ (r & C::SWZ)));
+        if (row0 + r < N) *(i32x4*)((uint8_t*)(out + (size_t)(row0 + r) * D) + 16 * c) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int V>
+using BIC = std::integral_constant<int, V>;
+
+// ------------------------------------------------------------------------------------------
+// dQ: parallel over 128-query blocks
+// ------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    bf16_t* __restrict__ dQ, int N, int numQB, float c2 /* scale*log2(e) */, float scale) {
+    using C = BwdCfg<D>;
+    constexpr int BR = 128;
+    constexpr int BC = kBwdRows;
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TB];
+    uint8_t* const sK[2] = {sK0, sK1};
+    uint8_t* const sV[2] = {sV0, sV1};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = w / numQB;
+    const int qi = w - bh * numQB;
+    const int qb = CAUSAL ? (numQB - 1 - qi) : qi;   // heaviest blocks first
+    const int q0 = qb * BR;
+    const int q0w = q0 + 32 * wave;
+    const int qrow = q0w + col;
+    const size_t head = (size_t)bh * N * D;
+
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, N * C::ROW, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, N * C::ROW, kBufferConfig);
+    TileAddr<D> ta;
+    ta.init(wave, lane);
+
+    bf16x8 qf[C::KSTEPS], df[C::KSTEPS];
+    load_resident<D>(qf, Q + head, qrow, N, h);
+    load_resident<D>(df, dO + head, qrow, N, h);
+    const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+    const float dlt = qrow < N ? Dl[(size_t)bh * N + qrow] : 0.f;
+
+    int nkb = (N + BC - 1) / BC;
+    if (CAUSAL) nkb = min(nkb, (min(q0 + BR, N) - 1) / BC + 1);
+    // blocks [0, nfull) need no mask for any query of the workgroup
+    const int nfull = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
+
+    f32x16 acc[C::DT];
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) acc[e] = f32x16{};
+    const int key8h = 8 * h;
+
+    auto step = [&](int j, auto b_c, auto mask_c) {
+        constexpr int B = decltype(b_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value != 0;
+        const int kb = j * BC;
+        if (j + 1 < nkb) {
+            ta.load(rK, sK[B ^ 1], kb + BC, wave);
+            ta.load(rV, sV[B ^ 1], kb + BC, wave);
+        }
+        // S^T = K Q^T and dP^T = V dO^T (keys x queries)
+        f32x16 st{}, dpt{};
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sK[B], s), qf[s], st, 0, 0, 0);
+            dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sV[B], s), df[s], dpt, 0, 0, 0);
+        }
+        // register i holds key kb + 16(i/8) + 8h + i%8 of query qrow
+        bf16x8 dsf[2];
+        const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kb - key8h;   // last visible key offset
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float p = fast_exp2(__builtin_fmaf(st[i], c2, -lse2));
+            if constexpr (MASK) p = (16 * (i / 8) + (i % 8)) > lim ? 0.f : p;
+            dsf[i / 8][i % 8] = (bf16_t)(p * (dpt[i] - dlt));
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sK[B], e, ch), dsf[ch], acc[e], 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    ta.load(rK, sK0, 0, wave);
+    ta.load(rV, sV0, 0, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int j = 0;
+    for (; j + 1 < nkb && j + 1 < nfull; j += 2) {
+        step(j, BIC<0>{}, BIC<0>{});
+        step(j + 1, BIC<1>{}, BIC<0>{});
+    }
+    for (; j < nkb; j += 2) {
+        if (j >= nfull) step(j, BIC<0>{}, BIC<1>{});
+        else step(j, BIC<0>{}, BIC<0>{});
+        if (j + 1 < nkb) step(j + 1, BIC<1>{}, BIC<1>{});
+    }
+
+    // dQ = scale dQ~ (each wave stages its tile in one of the four tile buffers)
+    uint8_t* const stg = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
+    store_rows<D>(acc, scale, stg, dQ + head, q0w, N, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV: parallel over 128-key blocks
+// ------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
+    using C = BwdCfg<D>;
+    constexpr int BK = 128;
+    constexpr int BQ = kBwdRows;
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ0[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ1[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sD0[C::TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sD1[C::TB];
+    uint8_t* const sQ[2] = {sQ0, sQ1};
+    uint8_t* const sD[2] = {sD0, sD1};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = w / numKB;
+    const int kbi = w - bh * numKB;   // causal: low key blocks see the most queries and come first
+    const int k0 = kbi * BK;
+    const int k0w = k0 + 32 * wave;
+    const int krow = k0w + col;
+    const size_t head = (size_t)bh * N * D;
+
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head), (short)0, N * C::ROW, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, N * C::ROW, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rDl = __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
+    TileAddr<D> ta;
+    ta.init(wave, lane);
+
+    bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+    load_resident<D>(kf, K + head, krow, N, h);
+    load_resident<D>(vf, V + head, krow, N, h);
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? min(k0, N) / BQ : 0;   // queries before the first key see none of it
+    f32x16 dk[C::DT], dv[C::DT];
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+        dk[e] = f32x16{};
+        dv[e] = f32x16{};
+    }
+
+    auto step = [&](int i, auto b_c, auto mask_c) {
+        constexpr int B = decltype(b_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value != 0;
+        const int q0 = i * BQ;
+        if (i + 1 < nqb) {
+            ta.load(rQ, sQ[B ^ 1], q0 + BQ, wave);
+            ta.load(rO, sD[B ^ 1], q0 + BQ, wave);
+        }
+        // logsumexp and D of the 16 queries of each 16-row chunk this lane half holds:
+        // rows q0 + 16u + 8h + 0..7
+        f32x4 lq[4], dq[4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v2 = 0; v2 < 2; ++v2) {
+                const int off = 4 * (q0 + 16 * u + 8 * h + 4 * v2);
+                lq[2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
+                dq[2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+            }
+        // S = Q K^T and dP = dO V^T (queries x keys)
+        f32x16 s{}, dp{};
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sQ[B], st), kf[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sD[B], st), vf[st], dp, 0, 0, 0);
+        }
+        // register r holds query q0 + 16(r/8) + 8h + r%8 of key krow
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float l2 = lq[r / 4][r % 4] * kLog2e;
+            float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
+            if constexpr (MASK) {
+                const int q = q0 + 16 * (r / 8) + 8 * h + (r % 8);
+                p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
+            }
+            pf[r / 8][r % 8] = (bf16_t)p;
+            dsf[r / 8][r % 8] = (bf16_t)(p * (dp[r] - dq[r / 4][r % 4]));
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e) {
+                dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sD[B], e, ch), pf[ch], dv[e], 0, 0, 0);
+                dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sQ[B], e, ch), dsf[ch], dk[e], 0, 0, 0);
+            }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    if (i0 < nqb) {
+        ta.load(rQ, sQ0, i0 * BQ, wave);
+        ta.load(rO, sD0, i0 * BQ, wave);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // query blocks that need a mask: the ones that reach below the last key of the
+        // workgroup (causal) and the ragged last one
+        const int nfree_hi = N / BQ;                                    // blocks [.., nfree_hi) are full
+        const int nfree_lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;   // blocks from here see all keys
+        int i = i0;
+        // (parity of the first block is 0 by construction: slot 0 was loaded above)
+        for (; i < nqb; i += 2) {
+            const bool m0 = i < nfree_lo || i >= nfree_hi;
+            const bool m1 = (i + 1) < nfree_lo || (i + 1) >= nfree_hi;
+            if (m0) step(i, BIC<0>{}, BIC<1>{});
+            else step(i, BIC<0>{}, BIC<0>{});
+            if (i + 1 < nqb) {
+                if (m1) step(i + 1, BIC<1>{}, BIC<1>{});
+                else step(i + 1, BIC<1>{}, BIC<0>{});
+            }
+        }
+    }
+
+    // dK = scale dK~, dV = dV~; each wave stages its tile in one of the four tile buffers
+    uint8_t* const stg = wave == 0 ? sQ0 : wave == 1 ? sQ1 : wave == 2 ? sD0 : sD1;
+    store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
+    store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
+}
+
+template <int D>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* delta, int BH, int N, float scale, bool causal,
+                      hipStream_t stream) {
+    const long long rows = (long long)BH * N;
+    {
+        constexpr int rows_per_block = (kBwdThreads / kWave) * (kWave / (D / 8));
+        const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, stream,
+                           (const bf16_t*)o, (const bf16_t*)dout, delta, rows);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float c2 = scale * kLog2e;
+    const int nb = (N + 127) / 128;
+    const long long total = (long long)BH * nb;
+    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+    const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)v, *dOb = (const bf16_t*)dout;
+    if (causal) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+                           dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+                           dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+                           dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+                           dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
+                           float scale, bool causal, hipStream_t stream) {
+    switch (d) {
+        case 64: return launch_bwd<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, N, scale, causal, stream);
+        case 128: return launch_bwd<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, BH, N, scale, causal, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module only draws inputs; it holds none of the attention arithmetic, and
 both the GPU path and the CPU oracle read the tensors it returns.
@@ -14,6 +14,8 @@ below have the shapes, sizes and value distributions of the benchmark cases):
   then the random +-1 sign vector of the Hadamard rotation is drawn as
   ``where(torch.rand(d, generator=g) > 0.5, 1, -1)``. The signs are the only
   random numbers the method itself uses, so they are an input here.
+- Backward workloads: the output gradient dO is the fourth iid N(0, 1) draw of the same
+  generator (after Q, K, V), cast to bfloat16.
 - The softmax scale is 1/sqrt(d) throughout.
 
 Layout is [B, H, N, d], contiguous.
@@ -85,6 +87,15 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16"):
     elif dtype not in ("f32", "fp8"):
         raise ValueError(f"unknown dtype {dtype}")
     return q, k, v
+
+
+def make_dout(B: int, H: int, N: int, d: int, seed: int):
+    """The output gradient dO of the backward workloads: iid N(0, 1), bfloat16, drawn after
+    Q, K, V from the same seeded generator (so Q, K, V equal those of ``make_qkv``)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    for _ in range(3):
+        torch.randn(B, H, N, d, dtype=torch.float32, generator=g)
+    return torch.randn(B, H, N, d, dtype=torch.float32, generator=g).to(torch.bfloat16)
 
 
 def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int):

@@ -1,5 +1,5 @@
 /*
- * fa.h - C ABI of the exact-attention forward pass for AMD Instinct MI355X (gfx950).
+ * fa.h - C ABI of exact attention (forward and backward) for AMD Instinct MI355X (gfx950).
  *
  * What it computes. For every batch b and head h, with Q, K, V the [N, d]
  * slices of that (b, h):
@@ -106,10 +106,12 @@ int fa_prep_fp8(const float* x, void* x8, float* s, const float* signs,
  * fa_fwd_fp8 - fused attention forward on E4M3 inputs with per-block scales.
  *
  * Source: "FlashAttention-3: How Warp Specialization ..." page, section 4:
- * the score tile is s_Q * s_K * (Q8 K8^T) with FP32 accumulation, the softmax
- * statistics and the output accumulator stay in high precision, and P is
- * converted to FP8 for the second product ("FlashAttention 2 & 3" page,
- * section "What stays in higher precision").
+ * the score tile is s_Q * s_K * (Q8 K8^T) with FP32 accumulation, and the
+ * softmax statistics and the output accumulator stay in high precision
+ * ("FlashAttention 2 & 3" page, section "What stays in higher precision").
+ * The pages also convert P to FP8 for the second product; this library keeps
+ * P (and V, expanded exactly from E4M3) in bfloat16 for it, since an E4M3 P
+ * costs an order of magnitude more output error on inputs with outliers.
  *
  *   q8, k8, v8  [B, H, N, d] E4M3 codes (as written by fa_prep_fp8; Q and K
  *               rotated with the same signs, V usually not rotated).
@@ -123,6 +125,30 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                const float* sq, const float* sk, const float* sv,
                void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, void* stream);
+
+/*
+ * fa_bwd - attention backward: the gradients of O = softmax(scale Q K^T [causal]) V.
+ *
+ * Source: "FlashAttention 2 & 3: Work Partitioning, Warp Specialization & FP8",
+ * section "The backward pass: recompute, and the one identity that makes it
+ * tile-able": P = exp(S - L) is rebuilt from the forward's logsumexp,
+ * dV = P^T dO, dP = dO V^T, D = rowsum(dO o O), dS = P o (dP - D),
+ * dQ = scale dS K, dK = scale dS^T Q. Three kernels on `stream`: D, then dK and dV
+ * (parallel over key blocks), then dQ (parallel over query blocks; no atomics,
+ * the result is deterministic).
+ *
+ *   q, k, v     [B, H, N, d] bfloat16, the forward's inputs.
+ *   o           [B, H, N, d] bfloat16, the forward's output.
+ *   dout        [B, H, N, d] bfloat16, the gradient of the loss with respect to o.
+ *   lse         [B, H, N] fp32, the forward's logsumexp (fa_fwd's lse).
+ *   dq, dk, dv  [B, H, N, d] bfloat16 (outputs). Must not overlap the inputs.
+ *   delta       [B, H, N] fp32 workspace owned by the caller (receives D).
+ *   d           64 or 128 (others: FA_ERR_HEADDIM).  dtype: FA_BF16 only
+ *               (others: FA_ERR_DTYPE).  scale, causal: as in the forward call.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /* fa_status_string - static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

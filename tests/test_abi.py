@@ -29,7 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_status_string", "fa_version"])
+    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string",
+                                           "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_version_and_status_strings(L):
     from exact_attention_06_amd import _lib
 
-    assert L.fa_version() == 100
+    assert L.fa_version() == 200
     for code, name in _lib.STATUS_NAMES.items():
         s = _lib.status_string(code)
         assert s and s != "unknown status", name
@@ -101,3 +102,24 @@ def test_python_binding_rejects_cpu_tensors(L):
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa_fwd(q, q, q, o=torch.empty_like(q), lse=torch.empty(1, 1, 64))
+
+
+def bwd(L, ptrs=None, B=1, H=1, N=128, d=128, scale=0.088, causal=0, dtype=1):
+    p = [P] * 10 if ptrs is None else ptrs
+    return L.fa_bwd(*p, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_bwd_argument_errors(L):
+    assert bwd(L, d=256) == -4          # the backward supports d = 64 and 128
+    assert bwd(L, d=96) == -4
+    assert bwd(L, dtype=0) == -5        # bfloat16 only
+    assert bwd(L, scale=0.0) == -6
+    assert bwd(L, causal=3) == -8
+    assert bwd(L, N=-1) == -3
+    for i in range(10):                 # q k v o dout lse dq dk dv delta
+        p = [P] * 10
+        p[i] = None
+        assert bwd(L, p) == -1, i
+        p[i] = P + 4
+        assert bwd(L, p) == -2, i
+    assert bwd(L, [None] * 10, N=0) == 0   # empty: nothing touched, nothing launched

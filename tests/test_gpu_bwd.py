@@ -1,0 +1,132 @@
+"""GPU parity of the attention backward (fa_bwd) against the float64 oracle, through the C ABI.
+
+Bound (each of dQ, dK, dV, bfloat16): the forward's bf16 output bound applied to every
+gradient, |dX_gpu - dX_ref| <= 1e-2 + 2^-8 |dX_ref| element-wise and mean |dX_gpu - dX_ref|
+<= 1e-3 (tests/_parity.py). The kernels round P and dS to bf16 before the second products
+(half an ulp, 2^-9 relative, per term, random) and the outputs to bf16 (another half ulp),
+and D is formed from the forward's bf16 O, the same rounding budget as the forward's output.
+
+The backward is run after the GPU forward (its O and LSE), as a caller would; one test feeds
+the oracle's O and LSE instead, so that the backward kernels are checked on their own. The
+oracle only ever sees Q, K, V and dO (the seeded inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_06_amd import fa_bwd, fa_fwd
+from exact_attention_06_amd.workloads import WORKLOADS, make_dout, make_qkv
+from oracle.attention import attention_fp64
+from oracle.attention_bwd import attention_bwd_fp64, attention_bwd_sampled_fp64
+from tests._parity import BF16_MAX_ABS, BF16_MEAN_ABS, o_err, o_excess, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run(q, k, v, do, causal, o=None, lse=None):
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    if o is None:
+        o, lse = fa_fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = fa_bwd(qd, kd, vd, o.cuda(), dod, lse.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(name, g, ref):
+    mx, mean = o_err(g, ref)
+    ex = o_excess(g, ref, BF16_MAX_ABS)
+    say(f"  {name}: max|d|={mx:.3g} (excess over bound {ex:.3g}) mean|d|={mean:.3g} max|ref|={np.abs(ref).max():.3g}")
+    assert ex <= 0 and mean <= BF16_MEAN_ABS, name
+    assert np.isfinite(to_np(g) if not isinstance(g, np.ndarray) else g).all(), name
+
+
+SHAPES = [  # (B, H, N, d): 32-row tiles, 128-row blocks, ragged tails, a single row
+    (1, 2, 64, 64), (2, 1, 257, 64), (1, 2, 300, 128), (1, 1, 1, 128), (1, 1, 33, 64),
+    (1, 2, 700, 128), (2, 2, 129, 128), (1, 1, 1000, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bwd_small_full_compare(shape, causal):
+    B, H, N, d = shape
+    say(f"bwd {shape} causal={causal}")
+    seed = 500 + N + d
+    q, k, v = make_qkv(B, H, N, d, seed)
+    do = make_dout(B, H, N, d, seed)
+    dq, dk, dv = run(q, k, v, do, causal)
+    rq, rk, rv = attention_bwd_fp64(q, k, v, do, d ** -0.5, causal)
+    for nm, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(nm, g, r)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_on_the_oracle_forward_outputs(causal):
+    B, H, N, d = 1, 2, 400, 128
+    say(f"bwd with the oracle's O and LSE, causal={causal}")
+    q, k, v = make_qkv(B, H, N, d, 77)
+    do = make_dout(B, H, N, d, 77)
+    o_ref, lse_ref = attention_fp64(q, k, v, d ** -0.5, causal)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref).to(torch.float32)
+    dq, dk, dv = run(q, k, v, do, causal, o, lse)
+    rq, rk, rv = attention_bwd_fp64(q, k, v, do, d ** -0.5, causal)
+    for nm, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(nm, g, r)
+
+
+@pytest.mark.parametrize("name,causal", [("b4h16n2k_d128", False), ("b4h16n2k_d128", True),
+                                         ("b4h16n8k_d128", False), ("b8h16n4k_d64", False)])
+def test_bwd_full_size_sampled(name, causal):
+    w = WORKLOADS[name]
+    say(f"bwd workload {name} causal={causal} (sampled rows)")
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.seed)
+    do = make_dout(w.B, w.H, w.N, w.d, w.seed)
+    dq, dk, dv = run(q, k, v, do, causal)
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+        rows = sample_rows(w.N, 64, seed=b * 100 + h)
+        cols = sample_rows(w.N, 64, seed=b * 100 + h + 7)
+        rq, rk, rv, _ = attention_bwd_sampled_fp64(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, causal, rows, cols)
+        ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+        check(f"dQ[{b},{h}]", to_np(dq[b, h][ri]), rq)
+        check(f"dK[{b},{h}]", to_np(dk[b, h][ci]), rk)
+        check(f"dV[{b},{h}]", to_np(dv[b, h][ci]), rv)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+def test_bwd_uniform_scores_closed_form():
+    """Q = 0: every query spreads uniformly, so dV_j = mean over queries of dO (non-causal),
+    and dK = scale dS^T Q = 0 (written out here, independent of the oracle)."""
+    B, H, N, d = 1, 2, 333, 128
+    say("bwd uniform scores")
+    _, k, v = make_qkv(B, H, N, d, 5)
+    do = make_dout(B, H, N, d, 5)
+    q = torch.zeros_like(k)
+    _, dk, dv = run(q, k, v, do, False)
+    mean_do = to_np(do).mean(axis=2, keepdims=True)
+    check("dV", dv, np.broadcast_to(mean_do, dv.shape))
+    check("dK", dk, np.zeros(dk.shape))
+
+
+def test_bwd_deterministic():
+    B, H, N, d = 2, 2, 500, 128
+    q, k, v = make_qkv(B, H, N, d, 9)
+    do = make_dout(B, H, N, d, 9)
+    a = run(q, k, v, do, True)
+    b = run(q, k, v, do, True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_empty_problem():
+    t = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda")
+    dq, dk, dv = fa_bwd(t, t, t, t, t, lse)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and dk.numel() == 0 and dv.numel() == 0
