@@ -15,7 +15,7 @@
 //    P^T = exp2(S^T c - L log2 e) and dS^T = P^T o (dP^T - D) stay in registers and are the B
 //    operand (bf16) of dQ^T += K^T dS^T, whose A operand K^T comes from the LDS transpose read.
 // 3. bwd_dkdv_kernel, parallel over 128-key blocks: each wave keeps K^T and V^T of its 32 keys
-//    in registers and streams 32-query blocks of Q and dO through LDS. S = Q K^T and
+//    in registers and streams 32- or 64-query blocks of Q and dO through LDS. S = Q K^T and
 //    dP = dO V^T put one key in each lane pair; P and dS (bf16) are the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T from the LDS transpose read.
 //
@@ -23,16 +23,25 @@
 // swap_bits23, so that result registers 8u .. 8u+7 of lane half h hold rows 16u + 8h + 0..7:
 // exactly the B operand of a 32x32x16 product over those 16 rows. Tiles are row-major bf16 in
 // LDS, loaded straight from HBM (buffer_load ... lds; rows past N read as zero), 16-byte
-// chunks XOR-swizzled by swap_bits23(row) like the forward's K tiles.
+// chunks XOR-swizzled (bwd_slot) so that both the row reads and the transposing reads are
+// free of bank conflicts.
 #include "fa_common.h"
-#include "fa_fwd_kernel.h"   // k_slot, kBufferConfig
+#include "fa_fwd_kernel.h"   // kBufferConfig
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
 constexpr int kBwdThreads = 256;   // 4 waves
-constexpr int kBwdRows = 32;       // rows per streamed tile (keys in dq, queries in dkdv)
+constexpr int kBwdRows = 32;       // rows per streamed tile of the dq kernel (keys)
+#ifndef FA_DKDV_ROWS
+#define FA_DKDV_ROWS 64
+#endif
+// queries per step of the dkdv kernel: two 32-query tiles at d = 128 (one wave per SIMD: the
+// second tile's products overlap the first tile's softmax); one at d = 64 (two waves per SIMD,
+// whose registers two tiles would exceed)
+template <int D>
+constexpr int dkdv_rows() { return D <= 64 ? 32 : FA_DKDV_ROWS; }
 
 // ------------------------------------------------------------------------------------------
 // D = rowsum(dO o O)
@@ -61,14 +70,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __
 // ------------------------------------------------------------------------------------------
 // shared pieces of the two MFMA kernels
 // ------------------------------------------------------------------------------------------
-template <int D>
+
+// 16-byte chunk swizzle of the streamed tiles, which are read both as MFMA rows (16 rows at
+// one chunk position) and by the transposing read (4 consecutive rows at 4 chunk positions
+// per half wave). f(r) = 2(r&3) ^ 8(r&1) ^ ((r>>2)&3): the first two terms (the forward's V
+// swizzle) make the transposing reads conflict-free, and they span a 2-dimensional subspace
+// of the 4 low chunk bits that the last term (constant within 4 consecutive rows)
+// complements, so f is a bijection on row & 15 for the row reads.
+template <int MASK>
+__device__ __forceinline__ int bwd_slot(int r, int c) {
+    return c ^ ((2 * (r & 3) ^ 8 * (r & 1) ^ ((r >> 2) & 3)) & MASK);
+}
+template <int D, int ROWS = kBwdRows>
 struct BwdCfg {
     static constexpr int ROW = D * 2;                    // bytes per bf16 row
     static constexpr int CPR = ROW / 16;                 // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
     static constexpr int KSTEPS = D / 16;                // 32x32x16 products over d
     static constexpr int DT = D / 32;                    // 32-wide d tiles of a transposed accumulator
-    static constexpr int TB = kBwdRows * ROW;            // bytes of one streamed tile
+    static constexpr int TB = ROWS * ROW;                // bytes of one streamed tile
     static constexpr int RPL = 1024 / ROW;               // rows per 1 KB DMA region
     static constexpr int LOADS = TB / 1024 / 4;          // DMA loads per thread per tile
     static_assert(LOADS >= 1, "tile must give every thread a load");
@@ -84,9 +104,9 @@ struct BwdCfg {
 //   the swizzle): lane (g, L) reads 8 bytes of row 8(g>>1) + (L>>2) (and the row 4 below),
 //   columns 32e + 16(g&1) + 4(L&3) .. +3, as ds_read_b64_tr_b16 expects.
 // - dma[i]: source offsets of the tile loads (load i of wave w fills 1 KB region w + 4i).
-template <int D>
+template <int D, int ROWS = kBwdRows>
 struct TileAddr {
-    using C = BwdCfg<D>;
+    using C = BwdCfg<D, ROWS>;
     int rd[C::KA];
     int trlo[C::EA], trhi[C::EA];
     int dma[C::LOADS];
@@ -94,29 +114,29 @@ struct TileAddr {
         const int h = lane >> 5, col = lane & 31;
         const int rr = swap_bits23(col);
 #pragma unroll
-        for (int s = 0; s < C::KA; ++s) rd[s] = rr * C::ROW + 16 * k_slot<C::SWZ>(rr, 2 * s + h);
+        for (int s = 0; s < C::KA; ++s) rd[s] = rr * C::ROW + 16 * bwd_slot<C::SWZ>(rr, 2 * s + h);
         const int g = lane >> 4, L = lane & 15;
         const int r0 = 8 * (g >> 1) + (L >> 2);
 #pragma unroll
         for (int e = 0; e < C::EA; ++e) {
             const int byte = 64 * e + 32 * (g & 1) + 8 * (L & 3);
-            trlo[e] = r0 * C::ROW + 16 * k_slot<C::SWZ>(r0, byte / 16) + (byte & 15);
-            trhi[e] = (r0 + 4) * C::ROW + 16 * k_slot<C::SWZ>(r0 + 4, byte / 16) + (byte & 15);
+            trlo[e] = r0 * C::ROW + 16 * bwd_slot<C::SWZ>(r0, byte / 16) + (byte & 15);
+            trhi[e] = (r0 + 4) * C::ROW + 16 * bwd_slot<C::SWZ>(r0 + 4, byte / 16) + (byte & 15);
         }
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) {
             const int r = C::RPL * (wave + 4 * i) + lane / C::CPR;
-            dma[i] = r * C::ROW + 16 * k_slot<C::SWZ>(r, lane % C::CPR);
+            dma[i] = r * C::ROW + 16 * bwd_slot<C::SWZ>(r, lane % C::CPR);
         }
     }
-    // 32 rows starting at row0 of the buffer r into tile dst
+    // ROWS rows starting at row0 of the buffer r into tile dst
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int row0, int wave) const {
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) lds_dma16(r, dst + 1024 * (wave + 4 * i), dma[i] + row0 * C::ROW);
     }
-    // A operand (32 rows x 16 d) of step s
-    __device__ __forceinline__ bf16x8 row_operand(const uint8_t* t, int s) const {
-        return *(const bf16x8*)(t + 256 * (s / C::KSPAN) + rd[s % C::KSPAN]);
+    // A operand (32 rows x 16 d) of step s, rows 32 tt .. 32 tt + 31 of the tile
+    __device__ __forceinline__ bf16x8 row_operand(const uint8_t* t, int s, int tt = 0) const {
+        return *(const bf16x8*)(t + 32 * tt * C::ROW + 256 * (s / C::KSPAN) + rd[s % C::KSPAN]);
     }
     // A operand (32 d x 16 rows) of d tile e and 16-row chunk ch, from the transposed read
     __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* t, int e, int ch) const {
@@ -280,14 +300,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 // ------------------------------------------------------------------------------------------
 // dK, dV: parallel over 128-key blocks
 // ------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int BQ>
 __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
-    using C = BwdCfg<D>;
+    using C = BwdCfg<D, BQ>;
     constexpr int BK = 128;
-    constexpr int BQ = kBwdRows;
+    constexpr int QT = BQ / 32;   // 32-query tiles per step
     __shared__ __attribute__((aligned(1024))) uint8_t sQ0[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sQ1[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sD0[C::TB];
@@ -311,7 +331,7 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
     const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, N * C::ROW, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rDl = __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
-    TileAddr<D> ta;
+    TileAddr<D, BQ> ta;
     ta.init(wave, lane);
 
     bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
@@ -335,45 +355,55 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
             ta.load(rQ, sQ[B ^ 1], q0 + BQ, wave);
             ta.load(rO, sD[B ^ 1], q0 + BQ, wave);
         }
-        // logsumexp and D of the 16 queries of each 16-row chunk this lane half holds:
-        // rows q0 + 16u + 8h + 0..7
-        f32x4 lq[4], dq[4];
+        // logsumexp and D of the queries this lane half holds: tile tt, rows
+        // q0 + 32 tt + 16u + 8h + 0..7
+        f32x4 lq[QT][4], dq[QT][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int tt = 0; tt < QT; ++tt)
 #pragma unroll
-            for (int v2 = 0; v2 < 2; ++v2) {
-                const int off = 4 * (q0 + 16 * u + 8 * h + 4 * v2);
-                lq[2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
-                dq[2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v2 = 0; v2 < 2; ++v2) {
+                    const int off = 4 * (q0 + 32 * tt + 16 * u + 8 * h + 4 * v2);
+                    lq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
+                    dq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+                }
+        // S = Q K^T and dP = dO V^T (queries x keys), per 32-query tile
+        f32x16 s[QT], dp[QT];
+#pragma unroll
+        for (int tt = 0; tt < QT; ++tt) {
+            s[tt] = f32x16{};
+            dp[tt] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < C::KSTEPS; ++st) {
+                s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sQ[B], st, tt), kf[st], s[tt], 0, 0, 0);
+                dp[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sD[B], st, tt), vf[st], dp[tt], 0, 0, 0);
             }
-        // S = Q K^T and dP = dO V^T (queries x keys)
-        f32x16 s{}, dp{};
-#pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sQ[B], st), kf[st], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sD[B], st), vf[st], dp, 0, 0, 0);
         }
-        // register r holds query q0 + 16(r/8) + 8h + r%8 of key krow
-        bf16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float l2 = lq[r / 4][r % 4] * kLog2e;
-            float p = fast_exp2(__builtin_fmaf(s[r], c2, -l2));
-            if constexpr (MASK) {
-                const int q = q0 + 16 * (r / 8) + 8 * h + (r % 8);
-                p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
+        for (int tt = 0; tt < QT; ++tt) {
+            // register r holds query q0 + 32 tt + 16(r/8) + 8h + r%8 of key krow
+            bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float l2 = lq[tt][r / 4][r % 4] * kLog2e;
+                float p = fast_exp2(__builtin_fmaf(s[tt][r], c2, -l2));
+                if constexpr (MASK) {
+                    const int q = q0 + 32 * tt + 16 * (r / 8) + 8 * h + (r % 8);
+                    p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
+                }
+                pf[r / 8][r % 8] = (bf16_t)p;
+                dsf[r / 8][r % 8] = (bf16_t)(p * (dp[tt][r] - dq[tt][r / 4][r % 4]));
             }
-            pf[r / 8][r % 8] = (bf16_t)p;
-            dsf[r / 8][r % 8] = (bf16_t)(p * (dp[r] - dq[r / 4][r % 4]));
+            // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries of tile tt
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int e = 0; e < C::DT; ++e) {
+                    dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sD[B], e, 2 * tt + ch), pf[ch], dv[e], 0, 0, 0);
+                    dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sQ[B], e, 2 * tt + ch), dsf[ch], dk[e], 0, 0, 0);
+                }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int e = 0; e < C::DT; ++e) {
-                dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sD[B], e, ch), pf[ch], dv[e], 0, 0, 0);
-                dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sQ[B], e, ch), dsf[ch], dk[e], 0, 0, 0);
-            }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
@@ -388,7 +418,7 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
         const int nfree_hi = N / BQ;                                    // blocks [.., nfree_hi) are full
         const int nfree_lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;   // blocks from here see all keys
         int i = i0;
-        // (parity of the first block is 0 by construction: slot 0 was loaded above)
+        // (the first block of each pair uses slot 0, which was loaded above)
         for (; i < nqb; i += 2) {
             const bool m0 = i < nfree_lo || i >= nfree_hi;
             const bool m1 = (i + 1) < nfree_lo || (i + 1) >= nfree_hi;
@@ -401,7 +431,7 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
         }
     }
 
-    // dK = scale dK~, dV = dV~; each wave stages its tile in one of the four tile buffers
+    // dK = scale dK~, dV = dV~; each wave stages its 32-key tile in one of the tile buffers
     uint8_t* const stg = wave == 0 ? sQ0 : wave == 1 ? sQ1 : wave == 2 ? sD0 : sD1;
     store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
     store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
@@ -427,12 +457,12 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)v, *dOb = (const bf16_t*)dout;
     if (causal) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, dkdv_rows<D>()>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, dkdv_rows<D>()>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
         hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
