@@ -259,7 +259,7 @@ def main():
             do = make_dout(wx.B, wx.H, wx.N, wx.d, wx.seed).cuda()
             o, lse = fa_fwd(q, k, v, causal=causal)
             dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-            delta = torch.empty((wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
+            delta = torch.empty((2, wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
             m = time_launches(torch, lambda: fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal), s2, w2, 100.0)
             extra[f"bwd_{name}{'_causal' if causal else ''}"] = {
                 "ms": round(m, 4), "TFLOP/s": round(2.5 * wx.flops(causal) / m / 1e9, 1)}

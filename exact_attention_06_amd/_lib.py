@@ -166,7 +166,7 @@ def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=F
 def fa_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scale=None, causal=False, stream=None):
     """Gradients (dq, dk, dv) of attention from the forward's inputs, output o, logsumexp
     lse and the output gradient dout; bfloat16 [B, H, N, d] tensors, lse float32 [B, H, N].
-    Outputs and the fp32 [B, H, N] workspace ``delta`` are allocated here unless given."""
+    Outputs and the fp32 [2, B, H, N] workspace ``delta`` are allocated here unless given."""
     B, H, N, d = _bhnd(q)
     for t in (k, v, o, dout):
         if t.shape != q.shape or t.dtype != torch.bfloat16:
@@ -178,7 +178,9 @@ def fa_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scal
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    if delta.dtype != torch.float32 or delta.numel() < 2 * B * H * N:
+        raise ValueError("delta must be a float32 workspace of 2*B*H*N elements")
     _require_gpu(q, k, v, o, dout, lse, dq, dk, dv, delta)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),

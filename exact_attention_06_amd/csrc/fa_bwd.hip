@@ -8,7 +8,8 @@
 // key blocks so that dK and dV accumulate locally, and names fp32 atomics or a separate pass
 // for dQ; this file takes the separate pass (deterministic, no atomics):
 //
-// 1. bwd_delta_kernel: D = rowsum(dO o O) in fp32, one row per group of d/8 lanes.
+// 1. bwd_delta_kernel: D = rowsum(dO o O) in fp32, one row per group of d/8 lanes, and the
+//    exp2 bias -LSE log2(e) of every row (both into the caller's workspace).
 // 2. bwd_dq_kernel, parallel over 128-query blocks (the forward's layout): each wave keeps
 //    Q^T and dO^T of its 32 queries in registers as MFMA B operands and streams 32-key blocks
 //    of K and V through LDS. S^T = K Q^T and dP^T = V dO^T put one query in each lane pair;
@@ -46,10 +47,14 @@ constexpr int dkdv_rows() { return D <= 64 ? 32 : FA_DKDV_ROWS; }
 // ------------------------------------------------------------------------------------------
 // D = rowsum(dO o O)
 // ------------------------------------------------------------------------------------------
+// also nl2 = -LSE log2(e), the exp2 bias of P = exp2(S c - LSE log2 e), read per query by the
+// dK / dV passes
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __restrict__ O,
                                                                 const bf16_t* __restrict__ dO,
-                                                                float* __restrict__ delta, long long rows) {
+                                                                const float* __restrict__ LSE,
+                                                                float* __restrict__ delta, float* __restrict__ nl2,
+                                                                long long rows) {
     constexpr int LPR = D / 8;           // lanes per row, 8 bf16 each
     constexpr int RPW = kWave / LPR;     // rows per wave
     const int lane = threadIdx.x & 63;
@@ -64,7 +69,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (c == 0 && row < rows) delta[row] = acc;
+    if (c == 0 && row < rows) {
+        delta[row] = acc;
+        nl2[row] = -LSE[row] * kLog2e;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -206,8 +214,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[C::TB];
-    uint8_t* const sK[2] = {sK0, sK1};
-    uint8_t* const sV[2] = {sV0, sV1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -243,20 +249,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int e = 0; e < C::DT; ++e) acc[e] = f32x16{};
     const int key8h = 8 * h;
 
-    auto step = [&](int j, auto b_c, auto mask_c) {
+    auto step = [&](int j, auto b_c, auto mask_c) __attribute__((always_inline)) {
         constexpr int B = decltype(b_c)::value;
         constexpr bool MASK = decltype(mask_c)::value != 0;
         const int kb = j * BC;
         if (j + 1 < nkb) {
-            ta.load(rK, sK[B ^ 1], kb + BC, wave);
-            ta.load(rV, sV[B ^ 1], kb + BC, wave);
+            ta.load(rK, (B ? sK0 : sK1), kb + BC, wave);
+            ta.load(rV, (B ? sV0 : sV1), kb + BC, wave);
         }
         // S^T = K Q^T and dP^T = V dO^T (keys x queries)
         f32x16 st{}, dpt{};
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sK[B], s), qf[s], st, 0, 0, 0);
-            dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sV[B], s), df[s], dpt, 0, 0, 0);
+            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sK1 : sK0), s), qf[s], st, 0, 0, 0);
+            dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sV1 : sV0), s), df[s], dpt, 0, 0, 0);
         }
         // register i holds key kb + 16(i/8) + 8h + i%8 of query qrow
         bf16x8 dsf[2];
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
             for (int e = 0; e < C::DT; ++e)
-                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sK[B], e, ch), dsf[ch], acc[e], 0, 0, 0);
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sK1 : sK0), e, ch), dsf[ch], acc[e], 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
@@ -300,10 +306,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 // ------------------------------------------------------------------------------------------
 // dK, dV: parallel over 128-key blocks
 // ------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int BQ>
-__global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(
+// MODE: 1 = dV only, 2 = dK only, 3 = both (one pass; at d = 128 that needs one wave per SIMD)
+template <int D, bool CAUSAL, int BQ, int MODE>
+__global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    const bf16_t* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ Dl,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
     using C = BwdCfg<D, BQ>;
     constexpr int BK = 128;
@@ -312,8 +319,6 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
     __shared__ __attribute__((aligned(1024))) uint8_t sQ1[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sD0[C::TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sD1[C::TB];
-    uint8_t* const sQ[2] = {sQ0, sQ1};
-    uint8_t* const sD[2] = {sD0, sD1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -329,14 +334,15 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
 
     const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head), (short)0, N * C::ROW, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, N * C::ROW, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(LSE + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(NL2 + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rDl = __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
     TileAddr<D, BQ> ta;
     ta.init(wave, lane);
 
+    constexpr bool DOV = (MODE & 1) != 0, DOK = (MODE & 2) != 0;
     bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
     load_resident<D>(kf, K + head, krow, N, h);
-    load_resident<D>(vf, V + head, krow, N, h);
+    if constexpr (DOK) load_resident<D>(vf, V + head, krow, N, h);
 
     const int nqb = (N + BQ - 1) / BQ;
     const int i0 = CAUSAL ? min(k0, N) / BQ : 0;   // queries before the first key see none of it
@@ -347,15 +353,15 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
         dv[e] = f32x16{};
     }
 
-    auto step = [&](int i, auto b_c, auto mask_c) {
+    auto step = [&](int i, auto b_c, auto mask_c) __attribute__((always_inline)) {
         constexpr int B = decltype(b_c)::value;
         constexpr bool MASK = decltype(mask_c)::value != 0;
         const int q0 = i * BQ;
         if (i + 1 < nqb) {
-            ta.load(rQ, sQ[B ^ 1], q0 + BQ, wave);
-            ta.load(rO, sD[B ^ 1], q0 + BQ, wave);
+            ta.load(rQ, (B ? sQ0 : sQ1), q0 + BQ, wave);
+            ta.load(rO, (B ? sD0 : sD1), q0 + BQ, wave);
         }
-        // logsumexp and D of the queries this lane half holds: tile tt, rows
+        // -LSE log2(e) and D of the queries this lane half holds: tile tt, rows
         // q0 + 32 tt + 16u + 8h + 0..7
         f32x4 lq[QT][4], dq[QT][4];
 #pragma unroll
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
                 for (int v2 = 0; v2 < 2; ++v2) {
                     const int off = 4 * (q0 + 32 * tt + 16 * u + 8 * h + 4 * v2);
                     lq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
-                    dq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+                    if constexpr (DOK) dq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
                 }
         // S = Q K^T and dP = dO V^T (queries x keys), per 32-query tile
         f32x16 s[QT], dp[QT];
@@ -376,8 +382,9 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
             dp[tt] = f32x16{};
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
-                s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sQ[B], st, tt), kf[st], s[tt], 0, 0, 0);
-                dp[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(sD[B], st, tt), vf[st], dp[tt], 0, 0, 0);
+                s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sQ1 : sQ0), st, tt), kf[st], s[tt], 0, 0, 0);
+                if constexpr (DOK)
+                    dp[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sD1 : sD0), st, tt), vf[st], dp[tt], 0, 0, 0);
             }
         }
 #pragma unroll
@@ -386,22 +393,23 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
             bf16x8 pf[2], dsf[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float l2 = lq[tt][r / 4][r % 4] * kLog2e;
-                float p = fast_exp2(__builtin_fmaf(s[tt][r], c2, -l2));
+                    float p = fast_exp2(__builtin_fmaf(s[tt][r], c2, lq[tt][r / 4][r % 4]));   // lq: -LSE log2 e
                 if constexpr (MASK) {
                     const int q = q0 + 32 * tt + 16 * (r / 8) + 8 * h + (r % 8);
                     p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
                 }
-                pf[r / 8][r % 8] = (bf16_t)p;
-                dsf[r / 8][r % 8] = (bf16_t)(p * (dp[tt][r] - dq[tt][r / 4][r % 4]));
+                if constexpr (DOV) pf[r / 8][r % 8] = (bf16_t)p;
+                if constexpr (DOK) dsf[r / 8][r % 8] = (bf16_t)(p * (dp[tt][r] - dq[tt][r / 4][r % 4]));
             }
             // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries of tile tt
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int e = 0; e < C::DT; ++e) {
-                    dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sD[B], e, 2 * tt + ch), pf[ch], dv[e], 0, 0, 0);
-                    dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sQ[B], e, 2 * tt + ch), dsf[ch], dk[e], 0, 0, 0);
+                    if constexpr (DOV)
+                        dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sD1 : sD0), e, 2 * tt + ch), pf[ch], dv[e], 0, 0, 0);
+                    if constexpr (DOK)
+                        dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sQ1 : sQ0), e, 2 * tt + ch), dsf[ch], dk[e], 0, 0, 0);
                 }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -414,27 +422,51 @@ __global__ __launch_bounds__(kBwdThreads, (D <= 64 ? 2 : 1)) void bwd_dkdv_kerne
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         // query blocks that need a mask: the ones that reach below the last key of the
-        // workgroup (causal) and the ragged last one
-        const int nfree_hi = N / BQ;                                    // blocks [.., nfree_hi) are full
-        const int nfree_lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;   // blocks from here see all keys
-        int i = i0;
-        // (the first block of each pair uses slot 0, which was loaded above)
-        for (; i < nqb; i += 2) {
-            const bool m0 = i < nfree_lo || i >= nfree_hi;
-            const bool m1 = (i + 1) < nfree_lo || (i + 1) >= nfree_hi;
-            if (m0) step(i, BIC<0>{}, BIC<1>{});
-            else step(i, BIC<0>{}, BIC<0>{});
-            if (i + 1 < nqb) {
-                if (m1) step(i + 1, BIC<1>{}, BIC<1>{});
-                else step(i + 1, BIC<1>{}, BIC<0>{});
+        // workgroup (causal: a masked prefix) and the ragged last one (a masked tail); the
+        // blocks in between run in a loop without branches, so that the accumulators keep
+        // their registers (branches between step variants inside the loop make the compiler
+        // copy them on every iteration). Block i uses tile slot (i - i0) & 1.
+        const int nfree_hi = N / BQ;                                              // full blocks end here
+        const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;   // blocks from here see all keys
+        const int hi = max(lo, nfree_hi);
+        auto run = [&](int a, int b, auto mask_c) __attribute__((always_inline)) {   // blocks [a, b), all masked or all not
+            if (a >= b) return;
+            if ((a - i0) & 1) step(a++, BIC<1>{}, mask_c);
+            for (; a + 1 < b; a += 2) {
+                step(a, BIC<0>{}, mask_c);
+                step(a + 1, BIC<1>{}, mask_c);
             }
-        }
+            if (a < b) step(a, BIC<0>{}, mask_c);
+        };
+        run(i0, lo, BIC<1>{});
+        run(lo, hi, BIC<0>{});
+        run(hi, nqb, BIC<1>{});
     }
 
     // dK = scale dK~, dV = dV~; each wave stages its 32-key tile in one of the tile buffers
     uint8_t* const stg = wave == 0 ? sQ0 : wave == 1 ? sQ1 : wave == 2 ? sD0 : sD1;
-    store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
-    store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
+    if constexpr (DOK) store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
+    if constexpr (DOV) store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
+}
+
+// dK and dV: one pass at d = 64; at d = 128 the two accumulators need more registers than two
+// waves per SIMD leave, and one wave per SIMD leaves the matrix cores idle most of the time,
+// so dV and dK run as two passes (S is recomputed once more: 5 products instead of 4)
+template <int D, bool CAUSAL>
+void launch_dkdv(const bf16_t* Qb, const bf16_t* Kb, const bf16_t* Vb, const bf16_t* dOb, const float* nl2,
+                 const float* delta, bf16_t* dk, bf16_t* dv, int N, int nb, long long total, float c2, float scale,
+                 hipStream_t stream) {
+#ifndef FA_BWD_FUSED_DKDV
+    if constexpr (D > 64) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 1>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
+                           Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 2>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
+                           Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
+        return;
+    }
+#endif
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, dkdv_rows<D>(), 3>), dim3((unsigned)total), dim3(kBwdThreads), 0,
+                       stream, Qb, Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
 }
 
 template <int D>
@@ -447,7 +479,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
         const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, stream,
-                           (const bf16_t*)o, (const bf16_t*)dout, delta, rows);
+                           (const bf16_t*)o, (const bf16_t*)dout, lse, delta, delta + rows, rows);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -457,13 +489,11 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)v, *dOb = (const bf16_t*)dout;
     if (causal) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, dkdv_rows<D>()>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
-                           dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
+        launch_dkdv<D, true>(Qb, Kb, Vb, dOb, delta + rows, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, total, c2, scale, stream);
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, dkdv_rows<D>()>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
-                           dOb, lse, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, c2, scale);
+        launch_dkdv<D, false>(Qb, Kb, Vb, dOb, delta + rows, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, total, c2, scale, stream);
         hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb, Vb,
                            dOb, lse, delta, (bf16_t*)dq, N, nb, c2, scale);
     }
