@@ -24,7 +24,9 @@ causal), the same count for every backend. Also reported:
   last-level cache flushed.
 
 ``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
-rocprofv3 byte counters); ``--only-headline`` skips the extra workloads.
+rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
+``--only-bwd`` times only the backward on the headline shape (for kernel traces
+of the backward kernels) and prints its own JSON line.
 """
 
 from __future__ import annotations
@@ -55,6 +57,7 @@ def parse_args():
     p.add_argument("--only-headline", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true")
+    p.add_argument("--only-bwd", action="store_true")
     return p.parse_args()
 
 
@@ -199,6 +202,29 @@ def main():
     from exact_attention_06_amd import fa_fwd, fa_fwd_fp8, fa_prep_fp8
     from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_inputs, make_qkv
 
+    def bwd_case(wx, causal, steps, warmup, ramp_ms):
+        """Backward (dQ, dK, dV) after one forward; FLOPs counted as the page's five products,
+        2.5x the forward's."""
+        from exact_attention_06_amd import fa_bwd
+        from exact_attention_06_amd.workloads import make_dout
+        q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
+        do = make_dout(wx.B, wx.H, wx.N, wx.d, wx.seed).cuda()
+        o, lse = fa_fwd(q, k, v, causal=causal)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        delta = torch.empty((2, wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
+        m = time_launches(torch, lambda: fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal),
+                          steps, warmup, ramp_ms)
+        progress(f"bwd {wx.name} causal={causal}: {m:.3f} ms")
+        return {"ms": round(m, 4), "TFLOP/s": round(2.5 * wx.flops(causal) / m / 1e9, 1)}
+
+    if args.only_bwd:
+        wb = WORKLOADS[HEADLINE]
+        r = bwd_case(wb, False, args.steps, args.warmup, 100.0)
+        print(json.dumps({"metric": "attention bwd TFLOP/s (2.5 x 4*B*H*N^2*d)", "value": r["TFLOP/s"],
+                          "unit": "TFLOP/s", "ms_per_step": r["ms"], "steps": args.steps,
+                          "config": {"workload": f"fa_bwd B={wb.B} H={wb.H} N={wb.N} d={wb.d} bf16 non-causal"}}))
+        return 0
+
     def bf16_case(w, causal, steps, warmup, ramp_ms=0.0):
         q, k, v = (x.cuda() for x in make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype))
         o = torch.empty_like(q)
@@ -249,22 +275,9 @@ def main():
             extra[f"{name}{'_causal' if causal else ''}"] = {
                 "ms": round(m, 4), "TFLOP/s": round(wx.flops(causal) / m / 1e9, 1)}
             progress(f"{name} causal={causal}: {m:.3f} ms")
-        # backward (dQ, dK, dV): FLOPs counted as the page's five products, 2.5x the forward
-        from exact_attention_06_amd import fa_bwd
-        from exact_attention_06_amd.workloads import make_dout
         for name, causal in [("b4h16n8k_d128", False), ("b4h16n8k_d128", True), ("b4h16n2k_d128", False),
-                             ("b8h16n4k_d64", False)]:
-            wx = WORKLOADS[name]
-            q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
-            do = make_dout(wx.B, wx.H, wx.N, wx.d, wx.seed).cuda()
-            o, lse = fa_fwd(q, k, v, causal=causal)
-            dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-            delta = torch.empty((2, wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
-            m = time_launches(torch, lambda: fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal), s2, w2, 100.0)
-            extra[f"bwd_{name}{'_causal' if causal else ''}"] = {
-                "ms": round(m, 4), "TFLOP/s": round(2.5 * wx.flops(causal) / m / 1e9, 1)}
-            progress(f"bwd {name} causal={causal}: {m:.3f} ms")
-            del q, k, v, do, o, lse, dq, dk, dv, delta
+                             ("b4h16n2k_d128", True), ("b8h16n4k_d64", False)]:
+            extra[f"bwd_{name}{'_causal' if causal else ''}"] = bwd_case(WORKLOADS[name], causal, s2, w2, 100.0)
         # FP8 path: prep of Q, K (rotated) and V, then the FP8 forward
         wf = WORKLOADS["fp8_b4h16n8k_d128"]
         q, k, v, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))

@@ -89,7 +89,7 @@ template <int MASK>
 __device__ __forceinline__ int bwd_slot(int r, int c) {
     return c ^ ((2 * (r & 3) ^ 8 * (r & 1) ^ ((r >> 2) & 3)) & MASK);
 }
-template <int D, int ROWS = kBwdRows>
+template <int D, int ROWS = kBwdRows, int W = 4>
 struct BwdCfg {
     static constexpr int ROW = D * 2;                    // bytes per bf16 row
     static constexpr int CPR = ROW / 16;                 // 16-byte chunks per row
@@ -98,7 +98,7 @@ struct BwdCfg {
     static constexpr int DT = D / 32;                    // 32-wide d tiles of a transposed accumulator
     static constexpr int TB = ROWS * ROW;                // bytes of one streamed tile
     static constexpr int RPL = 1024 / ROW;               // rows per 1 KB DMA region
-    static constexpr int LOADS = TB / 1024 / 4;          // DMA loads per thread per tile
+    static constexpr int LOADS = TB / 1024 / W;          // DMA loads per thread per tile (W waves)
     static_assert(LOADS >= 1, "tile must give every thread a load");
     static constexpr int KSPAN = 8;                      // steps per 16 chunks
     static constexpr int KA = KSTEPS < KSPAN ? KSTEPS : KSPAN;
@@ -111,10 +111,10 @@ struct BwdCfg {
 // - trlo[e] / trhi[e]: transposed reads of d tile e for the 16-row chunk 0 (rows 16 apart keep
 //   the swizzle): lane (g, L) reads 8 bytes of row 8(g>>1) + (L>>2) (and the row 4 below),
 //   columns 32e + 16(g&1) + 4(L&3) .. +3, as ds_read_b64_tr_b16 expects.
-// - dma[i]: source offsets of the tile loads (load i of wave w fills 1 KB region w + 4i).
-template <int D, int ROWS = kBwdRows>
+// - dma[i]: source offsets of the tile loads (load i of wave w fills 1 KB region w + W i).
+template <int D, int ROWS = kBwdRows, int W = 4>
 struct TileAddr {
-    using C = BwdCfg<D, ROWS>;
+    using C = BwdCfg<D, ROWS, W>;
     int rd[C::KA];
     int trlo[C::EA], trhi[C::EA];
     int dma[C::LOADS];
@@ -133,14 +133,14 @@ struct TileAddr {
         }
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i) {
-            const int r = C::RPL * (wave + 4 * i) + lane / C::CPR;
+            const int r = C::RPL * (wave + W * i) + lane / C::CPR;
             dma[i] = r * C::ROW + 16 * bwd_slot<C::SWZ>(r, lane % C::CPR);
         }
     }
     // ROWS rows starting at row0 of the buffer r into tile dst
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int row0, int wave) const {
 #pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) lds_dma16(r, dst + 1024 * (wave + 4 * i), dma[i] + row0 * C::ROW);
+        for (int i = 0; i < C::LOADS; ++i) lds_dma16(r, dst + 1024 * (wave + W * i), dma[i] + row0 * C::ROW);
     }
     // A operand (32 rows x 16 d) of step s, rows 32 tt .. 32 tt + 31 of the tile
     __device__ __forceinline__ bf16x8 row_operand(const uint8_t* t, int s, int tt = 0) const {
@@ -449,6 +449,171 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
     if constexpr (DOV) store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
 }
 
+// ------------------------------------------------------------------------------------------
+// dK, dV with wave pairs (d = 128)
+// ------------------------------------------------------------------------------------------
+// One 128-key block per workgroup of 8 waves; waves p and p + 4 share the keys k0 + 32p .. +31.
+// Wave p (the P wave) keeps K resident; for query block i it computes S = Q K^T, P and
+// dV^T += dO^T P, and leaves P (fp32, the lane layout of S) in LDS. Wave p + 4 (the dS wave)
+// keeps V resident and runs one block behind: dP = dO V^T for block i - 1, dS = P o (dP - D)
+// with the P its partner left, dK^T += Q^T dS. Four products per query block (two separate
+// dV and dK passes take five), every Q / dO tile is loaded once for both gradients, and each
+// wave holds one accumulator, so two waves fit on a SIMD. A tile is in use for three steps
+// (being loaded, read by the P waves, read by the dS waves): three slots each for Q and dO,
+// two P slots per pair. Masks (causal diagonal, ragged tail) act on P only: a masked P is 0,
+// and so is dS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ Dl,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
+    constexpr int W = 8;
+    constexpr int BQ = 32, BK = 128;
+    using C = BwdCfg<D, BQ, W>;
+    constexpr int TB = C::TB;          // one 32-row tile
+    constexpr int PT = 64 * 16 * 4;    // one P tile: 16 fp32 per lane, stored as 4 planes of 16 B per lane
+    constexpr int OQ = 0, OD = 3 * TB, OP = 6 * TB;
+    constexpr int LDS_BYTES = OP + 8 * PT;
+    static_assert(LDS_BYTES >= W * TB, "the output staging reuses the tile slots");
+    __shared__ __attribute__((aligned(1024))) uint8_t sm[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool pwave = wave < 4;
+    const int h = lane >> 5, col = lane & 31;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = w / numKB;
+    const int kbi = w - bh * numKB;   // causal: low key blocks see the most queries and come first
+    const int k0 = kbi * BK;
+    const int k0w = k0 + 32 * pair;
+    const int krow = k0w + col;
+    const size_t head = (size_t)bh * N * D;
+
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head), (short)0, N * C::ROW, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, N * C::ROW, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(NL2 + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rDl = __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
+    TileAddr<D, BQ, W> ta;
+    ta.init(wave, lane);
+
+    bf16x8 kv[C::KSTEPS];   // K (P wave) or V (dS wave) of the pair's 32 keys
+    load_resident<D>(kv, (pwave ? K : V) + head, krow, N, h);
+    f32x16 acc[C::DT];      // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) acc[e] = f32x16{};
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? min(k0, N) / BQ : 0;   // queries before the first key see none of it
+    uint8_t* const pbuf = sm + OP + 2 * PT * pair;
+    auto slot = [&](int i) __attribute__((always_inline)) { return (i - i0) % 3; };
+    auto load_tiles = [&](int i) __attribute__((always_inline)) {
+        const int t = slot(i);
+        ta.load(rQ, sm + OQ + TB * t, i * BQ, wave);
+        ta.load(rO, sm + OD + TB * t, i * BQ, wave);
+    };
+    // four values per lane from a per-query fp32 vector: registers 4v .. 4v+3 of tile rows
+    // q0 + 16(v/2) + 8h + 4(v%2) + 0..3
+    auto row_vals = [&](__amdgpu_buffer_rsrc_t r, int q0, f32x4 (&x)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            x[v] = __builtin_bit_cast(f32x4, buffer_load16(r, 4 * (q0 + 16 * (v / 2) + 8 * h + 4 * (v % 2))));
+    };
+
+    // P wave, query block i: register r of S holds query i BQ + 16(r/8) + 8h + r%8 of key krow
+    auto step_p = [&](int i, auto mask_c) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_c)::value != 0;
+        if (i + 1 < nqb) load_tiles(i + 1);
+        const int q0 = i * BQ;
+        const uint8_t* tq = sm + OQ + TB * slot(i);
+        const uint8_t* td = sm + OD + TB * slot(i);
+        f32x4 lq[4];   // -LSE log2(e)
+        row_vals(rL, q0, lq);
+        f32x16 sc{};
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(tq, st), kv[st], sc, 0, 0, 0);
+        bf16x8 pf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(__builtin_fmaf(sc[r], c2, lq[r / 4][r % 4]));
+            if constexpr (MASK) {
+                const int q = q0 + 16 * (r / 8) + 8 * h + (r % 8);
+                p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
+            }
+            sc[r] = p;
+            pf[r / 8][r % 8] = (bf16_t)p;
+        }
+        uint8_t* pb = pbuf + PT * (i & 1) + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(f32x4*)(pb + 1024 * j) = f32x4{sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]};
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(td, e, ch), pf[ch], acc[e], 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    // dS wave, query block i (one step after the P wave's)
+    auto step_ds = [&](int i) __attribute__((always_inline)) {
+        if (i + 2 < nqb) load_tiles(i + 2);
+        const int q0 = i * BQ;
+        const uint8_t* tq = sm + OQ + TB * slot(i);
+        const uint8_t* td = sm + OD + TB * slot(i);
+        f32x4 dl[4];   // D
+        row_vals(rDl, q0, dl);
+        f32x16 dp{};
+#pragma unroll
+        for (int st = 0; st < C::KSTEPS; ++st)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(td, st), kv[st], dp, 0, 0, 0);
+        const uint8_t* pb = pbuf + PT * (i & 1) + 16 * lane;
+        f32x4 pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[j] = *(const f32x4*)(pb + 1024 * j);
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsf[r / 8][r % 8] = (bf16_t)(pv[r / 4][r % 4] * (dp[r] - dl[r / 4][r % 4]));
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(tq, e, ch), dsf[ch], acc[e], 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    if (i0 < nqb) {
+        // both kinds of wave take part in every tile load and in every barrier: nqb - i0 + 1
+        // steps after the first load, the P waves' blocks in steps 0 .. nqb - i0 - 1, the dS
+        // waves' in steps 1 .. nqb - i0
+        load_tiles(i0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (pwave) {
+            // blocks that need a mask: the ones reaching below the last key of the workgroup
+            // (causal: a masked prefix) and the ragged last one (a masked tail); the blocks in
+            // between run in a loop without branches
+            const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
+            const int hi = max(lo, N / BQ);
+            for (int i = i0; i < lo; ++i) step_p(i, BIC<1>{});
+            for (int i = lo; i < hi; ++i) step_p(i, BIC<0>{});
+            for (int i = hi; i < nqb; ++i) step_p(i, BIC<1>{});
+            __syncthreads();
+        } else {
+            if (i0 + 1 < nqb) load_tiles(i0 + 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            for (int i = i0; i < nqb; ++i) step_ds(i);
+        }
+    }
+
+    // dV = dV~, dK = scale dK~; each wave stages its 32-key tile in its own 32-row slot
+    store_rows<D>(acc, pwave ? 1.f : scale, sm + TB * wave, (pwave ? dV : dK) + head, k0w, N, lane);
+}
+
 // dK and dV: one pass at d = 64; at d = 128 the two accumulators need more registers than two
 // waves per SIMD leave, and one wave per SIMD leaves the matrix cores idle most of the time,
 // so dV and dK run as two passes (S is recomputed once more: 5 products instead of 4)
@@ -456,17 +621,25 @@ template <int D, bool CAUSAL>
 void launch_dkdv(const bf16_t* Qb, const bf16_t* Kb, const bf16_t* Vb, const bf16_t* dOb, const float* nl2,
                  const float* delta, bf16_t* dk, bf16_t* dv, int N, int nb, long long total, float c2, float scale,
                  hipStream_t stream) {
-#ifndef FA_BWD_FUSED_DKDV
-    if constexpr (D > 64) {
+#if defined(FA_BWD_SPLIT_DKDV)
+    constexpr int kind = D > 64 ? 2 : 0;
+#elif defined(FA_BWD_FUSED_DKDV)
+    constexpr int kind = 0;
+#else
+    constexpr int kind = D > 64 ? 1 : 0;
+#endif
+    if constexpr (kind == 1) {
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(512), 0, stream, Qb, Kb, Vb,
+                           dOb, nl2, delta, dk, dv, N, nb, c2, scale);
+    } else if constexpr (kind == 2) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 1>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
                            Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 2>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
                            Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
-        return;
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, dkdv_rows<D>(), 3>), dim3((unsigned)total), dim3(kBwdThreads), 0,
+                           stream, Qb, Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
     }
-#endif
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, dkdv_rows<D>(), 3>), dim3((unsigned)total), dim3(kBwdThreads), 0,
-                       stream, Qb, Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
 }
 
 template <int D>
