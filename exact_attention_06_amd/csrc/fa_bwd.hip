@@ -459,9 +459,11 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 // with the P its partner left, dK^T += Q^T dS. Four products per query block (two separate
 // dV and dK passes take five), every Q / dO tile is loaded once for both gradients, and each
 // wave holds one accumulator, so two waves fit on a SIMD. A tile is in use for three steps
-// (being loaded, read by the P waves, read by the dS waves): three slots each for Q and dO,
-// two P slots per pair. Masks (causal diagonal, ragged tail) act on P only: a masked P is 0,
-// and so is dS.
+// (being loaded, read by the P waves, read by the dS waves): three slots each for Q, dO and
+// each pair's P, block i in slot (i - lo) mod 3. The unmasked blocks from lo on run unrolled
+// by three, so that every LDS address is a per-lane register plus an immediate; the few
+// masked blocks compute their slot at run time. Masks (causal diagonal, ragged tail) act on P
+// only: a masked P is 0, and so is dS.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     constexpr int TB = C::TB;          // one 32-row tile
     constexpr int PT = 64 * 16 * 4;    // one P tile: 16 fp32 per lane, stored as 4 planes of 16 B per lane
     constexpr int OQ = 0, OD = 3 * TB, OP = 6 * TB;
-    constexpr int LDS_BYTES = OP + 8 * PT;
+    constexpr int LDS_BYTES = OP + 12 * PT;
     static_assert(LDS_BYTES >= W * TB, "the output staging reuses the tile slots");
     __shared__ __attribute__((aligned(1024))) uint8_t sm[LDS_BYTES];
 
@@ -506,10 +508,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
 
     const int nqb = (N + BQ - 1) / BQ;
     const int i0 = CAUSAL ? min(k0, N) / BQ : 0;   // queries before the first key see none of it
-    uint8_t* const pbuf = sm + OP + 2 * PT * pair;
-    auto slot = [&](int i) __attribute__((always_inline)) { return (i - i0) % 3; };
-    auto load_tiles = [&](int i) __attribute__((always_inline)) {
-        const int t = slot(i);
+    // blocks [i0, lo) reach below the last key of the workgroup (causal: masked), blocks from
+    // lo on see all of its keys; blocks from N / BQ on are ragged (masked)
+    const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
+    const int hi = max(lo, N / BQ);
+    uint8_t* const pbuf = sm + OP + 3 * PT * pair;
+    auto slot = [&](int i) __attribute__((always_inline)) { return ((i - lo) % 3 + 3) % 3; };
+    auto load_tiles = [&](int i, int t) __attribute__((always_inline)) {
         ta.load(rQ, sm + OQ + TB * t, i * BQ, wave);
         ta.load(rO, sm + OD + TB * t, i * BQ, wave);
     };
@@ -521,13 +526,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             x[v] = __builtin_bit_cast(f32x4, buffer_load16(r, 4 * (q0 + 16 * (v / 2) + 8 * h + 4 * (v % 2))));
     };
 
-    // P wave, query block i: register r of S holds query i BQ + 16(r/8) + 8h + r%8 of key krow
-    auto step_p = [&](int i, auto mask_c) __attribute__((always_inline)) {
+    // P wave, query block i in slot SL (-1: computed here): register r of S holds query
+    // i BQ + 16(r/8) + 8h + r%8 of key krow
+    auto step_p = [&](int i, auto sl_c, auto mask_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value;
         constexpr bool MASK = decltype(mask_c)::value != 0;
-        if (i + 1 < nqb) load_tiles(i + 1);
+        const int t = SL >= 0 ? SL : slot(i);
+        if (i + 1 < nqb) load_tiles(i + 1, SL >= 0 ? (SL + 1) % 3 : slot(i + 1));
         const int q0 = i * BQ;
-        const uint8_t* tq = sm + OQ + TB * slot(i);
-        const uint8_t* td = sm + OD + TB * slot(i);
+        const uint8_t* tq = sm + OQ + TB * t;
+        const uint8_t* td = sm + OD + TB * t;
         f32x4 lq[4];   // -LSE log2(e)
         row_vals(rL, q0, lq);
         f32x16 sc{};
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             sc[r] = p;
             pf[r / 8][r % 8] = (bf16_t)p;
         }
-        uint8_t* pb = pbuf + PT * (i & 1) + 16 * lane;
+        uint8_t* pb = pbuf + PT * t + 16 * lane;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *(f32x4*)(pb + 1024 * j) = f32x4{sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]};
@@ -557,19 +565,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    // dS wave, query block i (one step after the P wave's)
-    auto step_ds = [&](int i) __attribute__((always_inline)) {
-        if (i + 2 < nqb) load_tiles(i + 2);
+    // dS wave, query block i in slot SL (one step after the P wave's)
+    auto step_ds = [&](int i, auto sl_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value;
+        const int t = SL >= 0 ? SL : slot(i);
+        if (i + 2 < nqb) load_tiles(i + 2, SL >= 0 ? (SL + 2) % 3 : slot(i + 2));
         const int q0 = i * BQ;
-        const uint8_t* tq = sm + OQ + TB * slot(i);
-        const uint8_t* td = sm + OD + TB * slot(i);
+        const uint8_t* tq = sm + OQ + TB * t;
+        const uint8_t* td = sm + OD + TB * t;
         f32x4 dl[4];   // D
         row_vals(rDl, q0, dl);
         f32x16 dp{};
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(td, st), kv[st], dp, 0, 0, 0);
-        const uint8_t* pb = pbuf + PT * (i & 1) + 16 * lane;
+        const uint8_t* pb = pbuf + PT * t + 16 * lane;
         f32x4 pv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[j] = *(const f32x4*)(pb + 1024 * j);
@@ -589,24 +599,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         // both kinds of wave take part in every tile load and in every barrier: nqb - i0 + 1
         // steps after the first load, the P waves' blocks in steps 0 .. nqb - i0 - 1, the dS
         // waves' in steps 1 .. nqb - i0
-        load_tiles(i0);
+        load_tiles(i0, slot(i0));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // each loop runs without branches between step variants (a branch there makes the
+        // compiler copy the accumulators on every iteration)
+        int i = i0;
         if (pwave) {
-            // blocks that need a mask: the ones reaching below the last key of the workgroup
-            // (causal: a masked prefix) and the ragged last one (a masked tail); the blocks in
-            // between run in a loop without branches
-            const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
-            const int hi = max(lo, N / BQ);
-            for (int i = i0; i < lo; ++i) step_p(i, BIC<1>{});
-            for (int i = lo; i < hi; ++i) step_p(i, BIC<0>{});
-            for (int i = hi; i < nqb; ++i) step_p(i, BIC<1>{});
+            for (; i < lo; ++i) step_p(i, BIC<-1>{}, BIC<1>{});
+            for (; i + 3 <= hi; i += 3) {
+                step_p(i, BIC<0>{}, BIC<0>{});
+                step_p(i + 1, BIC<1>{}, BIC<0>{});
+                step_p(i + 2, BIC<2>{}, BIC<0>{});
+            }
+            for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{});   // (masking blocks below hi is harmless)
             __syncthreads();
         } else {
-            if (i0 + 1 < nqb) load_tiles(i0 + 1);
+            if (i0 + 1 < nqb) load_tiles(i0 + 1, slot(i0 + 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            for (int i = i0; i < nqb; ++i) step_ds(i);
+            for (; i < lo; ++i) step_ds(i, BIC<-1>{});
+            for (; i + 3 <= nqb; i += 3) {
+                step_ds(i, BIC<0>{});
+                step_ds(i + 1, BIC<1>{});
+                step_ds(i + 2, BIC<2>{});
+            }
+            for (; i < nqb; ++i) step_ds(i, BIC<-1>{});
         }
     }
 
