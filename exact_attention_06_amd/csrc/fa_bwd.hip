@@ -453,16 +453,17 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 // dK, dV with wave pairs (d = 128)
 // ------------------------------------------------------------------------------------------
 // One 128-key block per workgroup of 8 waves; waves p and p + 4 share the keys k0 + 32p .. +31.
-// Wave p (the P wave) keeps K resident; for query block i it computes S = Q K^T, P and
-// dV^T += dO^T P, and leaves P (fp32, the lane layout of S) in LDS. Wave p + 4 (the dS wave)
+// Wave p (the P wave) keeps K resident; in step i it adds dV^T += dO^T P of block i - 1, then
+// computes S = Q K^T and P of block i and leaves P (fp32, the lane layout of S) in LDS, so its
+// exponentials overlap its partner's dK products. Wave p + 4 (the dS wave)
 // keeps V resident and runs one block behind: dP = dO V^T for block i - 1, dS = P o (dP - D)
 // with the P its partner left, dK^T += Q^T dS. Four products per query block (two separate
 // dV and dK passes take five), every Q / dO tile is loaded once for both gradients, and each
 // wave holds one accumulator, so two waves fit on a SIMD. A tile is in use for three steps
 // (being loaded, read by the P waves, read by the dS waves): three slots each for Q, dO and
-// each pair's P, block i in slot (i - lo) mod 3. The unmasked blocks from lo on run unrolled
-// by three, so that every LDS address is a per-lane register plus an immediate; the few
-// masked blocks compute their slot at run time. Masks (causal diagonal, ragged tail) act on P
+// each pair's P, block i in slot (i - u) mod 3. The unmasked blocks from u on run unrolled by
+// three, so that every LDS address is a per-lane register plus an immediate; the few masked
+// blocks (and the first) compute their slot at run time. Masks (causal diagonal, ragged tail) act on P
 // only: a masked P is 0, and so is dS.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
@@ -512,8 +513,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     // lo on see all of its keys; blocks from N / BQ on are ragged (masked)
     const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
     const int hi = max(lo, N / BQ);
+    const int u = max(lo, i0 + 1);   // first block of the unrolled loops (the first block is peeled)
     uint8_t* const pbuf = sm + OP + 3 * PT * pair;
-    auto slot = [&](int i) __attribute__((always_inline)) { return ((i - lo) % 3 + 3) % 3; };
+    auto slot = [&](int i) __attribute__((always_inline)) { return ((i - u) % 3 + 3) % 3; };
     auto load_tiles = [&](int i, int t) __attribute__((always_inline)) {
         ta.load(rQ, sm + OQ + TB * t, i * BQ, wave);
         ta.load(rO, sm + OD + TB * t, i * BQ, wave);
@@ -526,23 +528,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             x[v] = __builtin_bit_cast(f32x4, buffer_load16(r, 4 * (q0 + 16 * (v / 2) + 8 * h + 4 * (v % 2))));
     };
 
-    // P wave, query block i in slot SL (-1: computed here): register r of S holds query
-    // i BQ + 16(r/8) + 8h + r%8 of key krow
-    auto step_p = [&](int i, auto sl_c, auto mask_c) __attribute__((always_inline)) {
+    bf16x8 pf[2];   // P wave: P of the previous block, the B operand of its dV product
+    auto dv_update = [&](const uint8_t* td) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int e = 0; e < C::DT; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(td, e, ch), pf[ch], acc[e], 0, 0, 0);
+    };
+    // P wave, step i: dV of block i - 1 (unless FIRST), then S and P of query block i in slot
+    // SL (-1: computed here); register r of S holds query i BQ + 16(r/8) + 8h + r%8 of key krow
+    auto step_p = [&](int i, auto sl_c, auto mask_c, auto first_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value;
         constexpr bool MASK = decltype(mask_c)::value != 0;
+        constexpr bool FIRST = decltype(first_c)::value != 0;
         const int t = SL >= 0 ? SL : slot(i);
         if (i + 1 < nqb) load_tiles(i + 1, SL >= 0 ? (SL + 1) % 3 : slot(i + 1));
+        if constexpr (!FIRST) dv_update(sm + OD + TB * (SL >= 0 ? (SL + 2) % 3 : slot(i - 1)));
         const int q0 = i * BQ;
         const uint8_t* tq = sm + OQ + TB * t;
-        const uint8_t* td = sm + OD + TB * t;
         f32x4 lq[4];   // -LSE log2(e)
         row_vals(rL, q0, lq);
         f32x16 sc{};
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(tq, st), kv[st], sc, 0, 0, 0);
-        bf16x8 pf[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float p = fast_exp2(__builtin_fmaf(sc[r], c2, lq[r / 4][r % 4]));
@@ -557,11 +567,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *(f32x4*)(pb + 1024 * j) = f32x4{sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]};
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int e = 0; e < C::DT; ++e)
-                acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(td, e, ch), pf[ch], acc[e], 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
@@ -606,19 +611,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         // compiler copy the accumulators on every iteration)
         int i = i0;
         if (pwave) {
-            for (; i < lo; ++i) step_p(i, BIC<-1>{}, BIC<1>{});
+            step_p(i++, BIC<-1>{}, BIC<1>{}, BIC<1>{});
+            for (; i < u; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
             for (; i + 3 <= hi; i += 3) {
-                step_p(i, BIC<0>{}, BIC<0>{});
-                step_p(i + 1, BIC<1>{}, BIC<0>{});
-                step_p(i + 2, BIC<2>{}, BIC<0>{});
+                step_p(i, BIC<0>{}, BIC<0>{}, BIC<0>{});
+                step_p(i + 1, BIC<1>{}, BIC<0>{}, BIC<0>{});
+                step_p(i + 2, BIC<2>{}, BIC<0>{}, BIC<0>{});
             }
-            for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{});   // (masking blocks below hi is harmless)
+            // the rest (masking blocks below hi is harmless), then dV of the last block
+            for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
+            dv_update(sm + OD + TB * slot(nqb - 1));
             __syncthreads();
         } else {
             if (i0 + 1 < nqb) load_tiles(i0 + 1, slot(i0 + 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            for (; i < lo; ++i) step_ds(i, BIC<-1>{});
+            for (; i < u; ++i) step_ds(i, BIC<-1>{});
             for (; i + 3 <= nqb; i += 3) {
                 step_ds(i, BIC<0>{});
                 step_ds(i + 1, BIC<1>{});
