@@ -24,11 +24,12 @@
 // swap_bits23, so that result registers 8u .. 8u+7 of lane half h hold rows 16u + 8h + 0..7:
 // exactly the B operand of a 32x32x16 product over those 16 rows. Tiles are row-major bf16 in
 // LDS, loaded straight from HBM (buffer_load ... lds; rows past N read as zero), 16-byte
-// chunks XOR-swizzled (bwd_slot) so that both the row reads and the transposing reads are
+// chunks XOR-swizzled (tile_slot) so that both the row reads and the transposing reads are
 // free of bank conflicts.
 #include "fa_common.h"
 #include "fa_fwd_kernel.h"   // kBufferConfig
 #include "fa_internal.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -79,99 +80,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __
 // shared pieces of the two MFMA kernels
 // ------------------------------------------------------------------------------------------
 
-// 16-byte chunk swizzle of the streamed tiles, which are read both as MFMA rows (16 rows at
-// one chunk position) and by the transposing read (4 consecutive rows at 4 chunk positions
-// per half wave). f(r) = 2(r&3) ^ 8(r&1) ^ ((r>>2)&3): the first two terms (the forward's V
-// swizzle) make the transposing reads conflict-free, and they span a 2-dimensional subspace
-// of the 4 low chunk bits that the last term (constant within 4 consecutive rows)
-// complements, so f is a bijection on row & 15 for the row reads.
-template <int MASK>
-__device__ __forceinline__ int bwd_slot(int r, int c) {
-    return c ^ ((2 * (r & 3) ^ 8 * (r & 1) ^ ((r >> 2) & 3)) & MASK);
-}
-template <int D, int ROWS = kBwdRows, int W = 4>
-struct BwdCfg {
-    static constexpr int ROW = D * 2;                    // bytes per bf16 row
-    static constexpr int CPR = ROW / 16;                 // 16-byte chunks per row
-    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
-    static constexpr int KSTEPS = D / 16;                // 32x32x16 products over d
-    static constexpr int DT = D / 32;                    // 32-wide d tiles of a transposed accumulator
-    static constexpr int TB = ROWS * ROW;                // bytes of one streamed tile
-    static constexpr int RPL = 1024 / ROW;               // rows per 1 KB DMA region
-    static constexpr int LOADS = TB / 1024 / W;          // DMA loads per thread per tile (W waves)
-    static_assert(LOADS >= 1, "tile must give every thread a load");
-    static constexpr int KSPAN = 8;                      // steps per 16 chunks
-    static constexpr int KA = KSTEPS < KSPAN ? KSTEPS : KSPAN;
-    static constexpr int EA = DT < 4 ? DT : 4;           // 4 d tiles = 16 chunks
-};
-
-// Per-lane addresses inside a swizzled 32-row tile:
-// - rd[s]: A-operand row reads, row swap_bits23(col), chunk 2s + h (steps s and s+8 are 256
-//   bytes apart);
-// - trlo[e] / trhi[e]: transposed reads of d tile e for the 16-row chunk 0 (rows 16 apart keep
-//   the swizzle): lane (g, L) reads 8 bytes of row 8(g>>1) + (L>>2) (and the row 4 below),
-//   columns 32e + 16(g&1) + 4(L&3) .. +3, as ds_read_b64_tr_b16 expects.
-// - dma[i]: source offsets of the tile loads (load i of wave w fills 1 KB region w + W i).
-template <int D, int ROWS = kBwdRows, int W = 4>
-struct TileAddr {
-    using C = BwdCfg<D, ROWS, W>;
-    int rd[C::KA];
-    int trlo[C::EA], trhi[C::EA];
-    int dma[C::LOADS];
-    __device__ __forceinline__ void init(int wave, int lane) {
-        const int h = lane >> 5, col = lane & 31;
-        const int rr = swap_bits23(col);
-#pragma unroll
-        for (int s = 0; s < C::KA; ++s) rd[s] = rr * C::ROW + 16 * bwd_slot<C::SWZ>(rr, 2 * s + h);
-        const int g = lane >> 4, L = lane & 15;
-        const int r0 = 8 * (g >> 1) + (L >> 2);
-#pragma unroll
-        for (int e = 0; e < C::EA; ++e) {
-            const int byte = 64 * e + 32 * (g & 1) + 8 * (L & 3);
-            trlo[e] = r0 * C::ROW + 16 * bwd_slot<C::SWZ>(r0, byte / 16) + (byte & 15);
-            trhi[e] = (r0 + 4) * C::ROW + 16 * bwd_slot<C::SWZ>(r0 + 4, byte / 16) + (byte & 15);
-        }
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int r = C::RPL * (wave + W * i) + lane / C::CPR;
-            dma[i] = r * C::ROW + 16 * bwd_slot<C::SWZ>(r, lane % C::CPR);
-        }
-    }
-    // ROWS rows starting at row0 of the buffer r into tile dst
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int row0, int wave) const {
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) lds_dma16(r, dst + 1024 * (wave + W * i), dma[i] + row0 * C::ROW);
-    }
-    // A operand (32 rows x 16 d) of step s, rows 32 tt .. 32 tt + 31 of the tile
-    __device__ __forceinline__ bf16x8 row_operand(const uint8_t* t, int s, int tt = 0) const {
-        return *(const bf16x8*)(t + 32 * tt * C::ROW + 256 * (s / C::KSPAN) + rd[s % C::KSPAN]);
-    }
-    // A operand (32 d x 16 rows) of d tile e and 16-row chunk ch, from the transposed read
-    __device__ __forceinline__ bf16x8 tr_operand(const uint8_t* t, int e, int ch) const {
-        const uint8_t* base = t + 16 * ch * C::ROW + 256 * (e / 4);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, base + trlo[e % 4]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, base + trhi[e % 4]));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);   // whole-vector concatenation
-    }
-};
-
-// B operand of a wave's 32 resident rows (query or key `row`): 16 values of d per step,
-// [16 s + 8 h, +8); zeros past N
-template <int D>
-__device__ __forceinline__ void load_resident(bf16x8 (&f)[D / 16], const bf16_t* base, int row, int N, int h) {
-    const bool ok = row < N;
-    const bf16_t* p = base + (size_t)(ok ? row : 0) * D + 8 * h;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) f[s] = ok ? *(const bf16x8*)(p + 16 * s) : bf16x8{};
-}
-
 // Write a wave's transposed fp32 accumulator (lane = row col, register 4a+b of d tile e =
 // column 32e + 8a + 4h + b) as bf16 rows times `mult`, staged through the wave's LDS tile
 // `stg` (32 x d) so that the global stores are whole rows, 16 bytes per lane.
 template <int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mult, uint8_t* stg, bf16_t* out,
                                            int row0, int N, int lane) {
-    using C = BwdCfg<D>;
+    using C = TileCfg<D>;
     const int h = lane >> 5, col = lane & 31;
 #pragma unroll
     for (int e = 0; e < C::DT; ++e)
@@ -207,7 +122,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     bf16_t* __restrict__ dQ, int N, int numQB, float c2 /* scale*log2(e) */, float scale) {
-    using C = BwdCfg<D>;
+    using C = TileCfg<D>;
     constexpr int BR = 128;
     constexpr int BC = kBwdRows;
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TB];
@@ -312,7 +227,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ Dl,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
-    using C = BwdCfg<D, BQ>;
+    using C = TileCfg<D, BQ>;
     constexpr int BK = 128;
     constexpr int QT = BQ / 32;   // 32-query tiles per step
     __shared__ __attribute__((aligned(1024))) uint8_t sQ0[C::TB];
@@ -472,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
     constexpr int W = 8;
     constexpr int BQ = 32, BK = 128;
-    using C = BwdCfg<D, BQ, W>;
+    using C = TileCfg<D, BQ, W>;
     constexpr int TB = C::TB;          // one 32-row tile
     constexpr int PT = 64 * 16 * 4;    // one P tile: 16 fp32 per lane, stored as 4 planes of 16 B per lane
     constexpr int OQ = 0, OD = 3 * TB, OP = 6 * TB;
