@@ -21,12 +21,14 @@ causal), the same count for every backend. Also reported:
   other workloads (including the FP8 path: rotation/quantisation of Q, K, V plus
   the FP8 forward) and the FP8 quantiser's HBM throughput; the tiny fp32 case and
   the short-sequence sweep in GB/s of algorithmic bytes, warm and with the
-  last-level cache flushed.
+  last-level cache flushed; split-key decoding (one new token against a key/value
+  cache) in GB/s of algorithmic bytes (K and V read once, Q read, O and LSE written).
 
 ``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
 rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
 ``--only-bwd`` times only the backward on the headline shape (for kernel traces
-of the backward kernels) and prints its own JSON line.
+of the backward kernels) and prints its own JSON line; ``--only-decode`` does the
+same for split-key decoding on the grouped-head 8K-cache workload.
 """
 
 from __future__ import annotations
@@ -58,6 +60,7 @@ def parse_args():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--only-bwd", action="store_true")
+    p.add_argument("--only-decode", action="store_true")
     return p.parse_args()
 
 
@@ -217,6 +220,30 @@ def main():
         progress(f"bwd {wx.name} causal={causal}: {m:.3f} ms")
         return {"ms": round(m, 4), "TFLOP/s": round(2.5 * wx.flops(causal) / m / 1e9, 1)}
 
+    def decode_case(wd, steps, warmup, ramp_ms):
+        from exact_attention_06_amd import fa_decode, fa_decode_workspace_size
+        from exact_attention_06_amd.workloads import make_decode_inputs
+        q, k, v = (x.cuda() for x in make_decode_inputs(wd.B, wd.Hq, wd.Hkv, wd.Nq, wd.Nk, wd.d, wd.seed))
+        o = torch.empty_like(q)
+        lse = torch.empty((wd.B, wd.Hq, wd.Nq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(16, fa_decode_workspace_size(wd.B, wd.Hq, wd.Hkv, wd.Nq, wd.Nk, wd.d)),
+                         dtype=torch.uint8, device="cuda")
+        m = time_launches(torch, lambda: fa_decode(q, k, v, o, lse, ws, causal=wd.causal), steps, warmup, ramp_ms)
+        nb = wd.kv_bytes()
+        progress(f"decode {wd.name}: {m:.4f} ms, {nb / m / 1e6:.0f} GB/s")
+        return {"ms": round(m, 4), "bytes": nb, "GB/s": round(nb / m / 1e6, 1),
+                "frac_of_8TBs": round(nb / m / 1e6 / PEAK_HBM_GBS, 4)}
+
+    if args.only_decode:
+        from exact_attention_06_amd.workloads import DECODE_WORKLOADS
+        wd = DECODE_WORKLOADS["decode_b16_hq32_hkv8_nk8k_d128"]
+        r = decode_case(wd, args.steps, args.warmup, 100.0)
+        print(json.dumps({"metric": "decode HBM GB/s (K, V read once; Q, O, LSE)", "value": r["GB/s"], "unit": "GB/s",
+                          "ms_per_step": r["ms"], "steps": args.steps,
+                          "config": {"workload": f"fa_decode B={wd.B} Hq={wd.Hq} Hkv={wd.Hkv} Nq={wd.Nq} "
+                                                 f"Nk={wd.Nk} d={wd.d} bf16"}}))
+        return 0
+
     if args.only_bwd:
         wb = WORKLOADS[HEADLINE]
         r = bwd_case(wb, False, args.steps, args.warmup, 100.0)
@@ -320,6 +347,9 @@ def main():
             progress(f"{name}: warm {warm['median']:.4f} ms, cold {cold['median']:.4f} ms")
             del q, k, v, o, lse
         del scratch
+        from exact_attention_06_amd.workloads import DECODE_WORKLOADS
+        for name in ("decode_b16_hq32_hkv8_nk8k_d128", "decode_b2_h32_nk32k_d128"):
+            extra[name] = decode_case(DECODE_WORKLOADS[name], args.steps, args.warmup, 100.0)
         result["extra"] = extra
     # calibration GEMM (hipBLASLt via torch): what a plain bf16 GEMM sustains on this GPU now
     a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")

@@ -23,7 +23,8 @@ STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_ALIGN", -3: "FA_ERR_SHAPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_decode_workspace_size", "fa_decode",
+            "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -53,6 +54,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_fp8.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     L.fa_bwd.restype = i
+    L.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_workspace_size.restype = ctypes.c_size_t
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+    L.fa_decode.restype = i
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -186,3 +191,33 @@ def fa_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scal
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         _ptr(delta), B, H, N, d, scale, int(bool(causal)), FA_BF16, _stream(stream)))
     return dq, dk, dv
+
+
+def fa_decode_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    """Bytes of fp32 workspace fa_decode needs for this shape (0: none)."""
+    return int(lib().fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fa_decode(q, k, v, o=None, lse=None, workspace=None, *, scale=None, causal=False, want_lse=True, stream=None):
+    """Decoding attention: q [B, Hq, Nq, d] against the key/value cache k, v [B, Hkv, Nk, d]
+    (bfloat16; Hkv divides Hq), split over the keys. Returns (o, lse); o is bfloat16
+    [B, Hq, Nq, d], lse float32 [B, Hq, Nq]. The workspace (uint8 or float32 GPU tensor of at
+    least fa_decode_workspace_size(...) bytes) is allocated here unless given."""
+    B, Hq, Nq, d = _bhnd(q)
+    Bk, Hkv, Nk, dk = _bhnd(k)
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with the batch and head dim of q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("fa_decode takes bfloat16 tensors")
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _require_gpu(q, k, v, o, lse, workspace)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
+                           int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(stream)))
+    return o, lse

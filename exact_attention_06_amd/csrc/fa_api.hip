@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;   // 0.2.0: fa_bwd
+constexpr int kVersion = 300;   // 0.3.0: fa_decode
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -26,6 +26,19 @@ int check_common(int B, int H, int N, int d, float scale, int causal) {
     const long long rows = (long long)B * H * (long long)N;
     if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
     if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+// decode shapes: returns FA_OK or the first error
+int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal) {
+    if (B < 0 || Hq < 0 || Hkv < 1 || Nq < 0 || Nk < 0 || Hq % Hkv != 0 || Nq > Nk) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_SCALE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    // rows of q / o and of the key/value cache fit int32, one head of K or V fits a buffer range
+    if ((long long)B * Hq * (long long)Nq > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)B * Hkv * (long long)Nk > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)Nk * d * 2 > 0x7fffffffLL) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -88,17 +101,41 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (check_decode(B, Hq, Hkv, Nq, Nk, d, 1.f, 0) != FA_OK) return 0;
+    if ((long long)B * Hq * Nq == 0) return 0;
+    return fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).ws_bytes;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+              int Nk, int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    int st = check_decode(B, Hq, Hkv, Nq, Nk, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((long long)B * Hq * Nq == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    const size_t need = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).ws_bytes;
+    if (need > 0 && !workspace) return FA_ERR_NULLPTR;
+    if (workspace_bytes < need) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+        (workspace && !aligned16(workspace)))
+        return FA_ERR_ALIGN;
+    return from_hip(fa::launch_decode_bf16(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULLPTR: return "a required pointer is NULL";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case FA_ERR_SHAPE: return "invalid shape (negative size, too many rows, or N*d*4 >= 2^31)";
-        case FA_ERR_HEADDIM: return "unsupported head dimension (64, 128 or 256; the backward: 64 or 128)";
+        case FA_ERR_HEADDIM: return "unsupported head dimension (64, 128 or 256; the backward and decoding: 64 or 128)";
         case FA_ERR_DTYPE: return "unsupported dtype";
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_LAUNCH: return "kernel launch failed";
-        case FA_ERR_ARG: return "invalid argument";
+        case FA_ERR_ARG: return "invalid argument (causal not 0/1, or a workspace smaller than required)";
         default: return "unknown status";
     }
 }

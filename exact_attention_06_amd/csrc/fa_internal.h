@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 namespace fa {
 
 // bf16 Q, K, V, O [BH, N, d]; lse [BH, N] or null. d in {64, 128, 256}.
@@ -28,5 +30,19 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream);
+
+// Split-key decoding: how the keys are cut (the same for a given shape, so that the caller's
+// workspace size can be asked for first). ncg column groups of 32 query rows, ntiles 32-key
+// tiles, tps tiles per split, nsplit splits; ws_bytes of fp32 workspace (0 with one split).
+struct DecodePlan {
+    int ncg, ntiles, tps, nsplit;
+    size_t ws_bytes;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+// bf16 q [B, Hq, Nq, d], k, v [B, Hkv, Nk, d] -> o [B, Hq, Nq, d] bf16, lse [B, Hq, Nq] or null;
+// ws: decode_plan(...).ws_bytes of workspace. d in {64, 128}.
+hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, int B,
+                              int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
 
 }  // namespace fa

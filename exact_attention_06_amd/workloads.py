@@ -16,6 +16,8 @@ below have the shapes, sizes and value distributions of the benchmark cases):
   random numbers the method itself uses, so they are an input here.
 - Backward workloads: the output gradient dO is the fourth iid N(0, 1) draw of the same
   generator (after Q, K, V), cast to bfloat16.
+- Decoding workloads: Q [B, Hq, Nq, d], then K and V [B, Hkv, Nk, d] (the key/value cache),
+  iid N(0, 1) from one seeded generator in that order, cast to bfloat16.
 - The softmax scale is 1/sqrt(d) throughout.
 
 Layout is [B, H, N, d], contiguous.
@@ -71,6 +73,55 @@ WORKLOADS = {
     + [Workload(f"short_b64h16n{n}_d128", 64, 16, n, 128, "bf16", (False,), 8,
                 f"short-sequence sweep, N={n} (bound by HBM)") for n in (128, 256, 512)]
 }
+
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A few query positions (Nq) against a key/value cache of Nk positions; Hkv key/value
+    heads shared by groups of Hq / Hkv query heads."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic HBM bytes: K and V read once, Q read, O and LSE written (bf16, fp32 LSE)."""
+        return (2 * self.B * self.Hkv * self.Nk * self.d * 2 + 2 * self.B * self.Hq * self.Nq * self.d * 2
+                + 4 * self.B * self.Hq * self.Nq)
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode_b16_hq32_hkv8_nk8k_d128", 16, 32, 8, 1, 8192, 128, False, 9,
+                       "one new token per sequence, grouped heads (4 query heads per key/value head), 8K cache"),
+        DecodeWorkload("decode_b2_h32_nk32k_d128", 2, 32, 32, 1, 32768, 128, False, 10,
+                       "one new token per sequence, one key/value head per query head, 32K cache"),
+        DecodeWorkload("decode_b16_hq32_hkv8_nq4_nk8k_d128", 16, 32, 8, 4, 8192, 128, True, 11,
+                       "four new positions per sequence under the causal mask (parity case)"),
+    ]
+}
+
+
+def make_decode_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int):
+    """Q [B, Hq, Nq, d], K and V [B, Hkv, Nk, d], iid N(0, 1) drawn in that order, bfloat16."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, Hq, Nq, d, dtype=torch.float32, generator=g)
+    k = torch.randn(B, Hkv, Nk, d, dtype=torch.float32, generator=g)
+    v = torch.randn(B, Hkv, Nk, d, dtype=torch.float32, generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
 
 OUTLIER_FRACTION = 0.001
 OUTLIER_FACTOR = 20.0

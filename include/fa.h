@@ -22,7 +22,7 @@
  * Conventions for every entry point:
  * - Tensors are dense, contiguous, row-major [B, H, N, d] ("BHND": batch, head,
  *   sequence, head dim); LSE is [B, H, N] fp32. Queries and keys have the same
- *   length N.
+ *   length N (fa_decode: Nq queries against Nk keys, with its own layout).
  * - Pointers are device pointers (HIP device memory) owned by the caller. The
  *   library never allocates, frees or copies host memory, and never
  *   synchronises: work is enqueued on `stream` (a hipStream_t passed as void*,
@@ -40,6 +40,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -150,6 +151,39 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_decode - attention of a few query positions against a long key/value
+ * sequence (autoregressive decoding), split over the keys.
+ *
+ * Source: "FlashAttention 2 & 3: Work Partitioning, Warp Specialization & FP8",
+ * the paragraph on the decode regime (FlashDecoding): the key/value sequence is
+ * split across the compute units, each part computes a partial softmax state
+ * (m, l, O~) and the parts are merged with the online-softmax combine of
+ * "FlashAttention-3 & GPU Kernel Optimization", section "Online softmax tiling
+ * mathematics". Grouped-query attention as in the flash_attn example of "Learn:
+ * The Memory Wall & FlashAttention": Hkv divides Hq and query head h reads
+ * key/value head h / (Hq / Hkv); the query heads of one group are computed
+ * together, so K and V are read once per group.
+ *
+ *   q         [B, Hq, Nq, d] bfloat16: the last Nq positions of each sequence.
+ *   k, v      [B, Hkv, Nk, d] bfloat16 (the key/value cache), Nq <= Nk.
+ *   o         [B, Hq, Nq, d] bfloat16 (output).
+ *   lse       [B, Hq, Nq] fp32 natural-log logsumexp (output), or NULL.
+ *   causal    0: every query sees all Nk keys. 1: query i (0-based among the Nq)
+ *             sees keys j <= Nk - Nq + i, the forward's mask when Nq = Nk.
+ *   workspace fp32 scratch owned by the caller, at least
+ *             fa_decode_workspace_size(...) bytes, 16-byte aligned; may be NULL
+ *             when that size is 0. Its contents are overwritten; calls that share
+ *             one workspace must not overlap in time.
+ *   d 64 or 128 (others: FA_ERR_HEADDIM); dtype FA_BF16 only (FA_ERR_DTYPE);
+ *   Hkv < 1, Hq not a multiple of Hkv, Nq > Nk: FA_ERR_SHAPE; workspace_bytes
+ *   below the required size: FA_ERR_ARG.
+ */
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* fa_status_string - static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

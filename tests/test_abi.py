@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_status_string",
-                                           "fa_version"])
+    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_decode_workspace_size",
+                                           "fa_decode", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_version_and_status_strings(L):
     from exact_attention_06_amd import _lib
 
-    assert L.fa_version() == 200
+    assert L.fa_version() == 300
     for code, name in _lib.STATUS_NAMES.items():
         s = _lib.status_string(code)
         assert s and s != "unknown status", name
@@ -123,3 +123,47 @@ def test_bwd_argument_errors(L):
         p[i] = P + 4
         assert bwd(L, p) == -2, i
     assert bwd(L, [None] * 10, N=0) == 0   # empty: nothing touched, nothing launched
+
+
+def dec(L, ptrs=None, B=2, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128, scale=0.088, causal=0, dtype=1, ws_bytes=None):
+    p = [P] * 5 if ptrs is None else ptrs[:5]
+    ws = P if ptrs is None else ptrs[5]
+    if ws_bytes is None:
+        ws_bytes = L.fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    return L.fa_decode(*p, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, ws, ws_bytes, None)
+
+
+def test_decode_workspace_size(L):
+    # split over the keys: one fp32 state (d values, max, sum) per split and query row
+    n = L.fa_decode_workspace_size(2, 8, 2, 1, 4096, 128)
+    assert n > 0 and n % (4 * (128 + 2)) == 0
+    rows = 2 * 8 * 1
+    assert (n // (4 * (128 + 2))) % rows == 0          # whole splits of every row
+    assert L.fa_decode_workspace_size(2, 8, 2, 1, 64, 128) == 0      # two tiles: one split, no workspace
+    assert L.fa_decode_workspace_size(2, 8, 3, 1, 4096, 128) == 0    # invalid shape
+    assert L.fa_decode_workspace_size(0, 8, 2, 1, 4096, 128) == 0    # empty
+
+
+def test_decode_argument_errors(L):
+    assert dec(L, d=256) == -4
+    assert dec(L, dtype=0) == -5
+    assert dec(L, scale=float("nan")) == -6
+    assert dec(L, causal=2) == -8
+    assert dec(L, Hkv=3) == -3            # Hkv must divide Hq
+    assert dec(L, Hkv=0) == -3
+    assert dec(L, Nq=5, Nk=4) == -3       # more queries than keys
+    need = L.fa_decode_workspace_size(2, 8, 2, 1, 4096, 128)
+    assert dec(L, ws_bytes=need - 1) == -8
+    for i in range(4):                    # q k v o
+        p = [P] * 6
+        p[i] = None
+        assert dec(L, p) == -1, i
+        p[i] = P + 4
+        assert dec(L, p) == -2, i
+    p = [P] * 6
+    p[4] = None                           # lse is optional: only the other checks apply
+    p[5] = P + 8
+    assert dec(L, p) == -2                # misaligned workspace
+    p[5] = None
+    assert dec(L, p) == -1                # the workspace is required when its size is > 0
+    assert dec(L, [None] * 6, Nq=0) == 0  # empty: nothing touched, nothing launched
