@@ -22,7 +22,9 @@ causal), the same count for every backend. Also reported:
   the FP8 forward) and the FP8 quantiser's HBM throughput; the tiny fp32 case and
   the short-sequence sweep in GB/s of algorithmic bytes, warm and with the
   last-level cache flushed; split-key decoding (one new token against a key/value
-  cache) in GB/s of algorithmic bytes (K and V read once, Q read, O and LSE written).
+  cache) in GB/s of algorithmic bytes (K and V read once, Q read, O and LSE written); the
+  forward with grouped key/value heads, a sliding window and packed sequences, in TFLOP/s
+  of the (query, key) pairs each query sees (4 d FLOPs per pair).
 
 ``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
 rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
@@ -94,6 +96,22 @@ def read_traffic():
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def visible_pairs(n: int, causal: bool, left: int, right: int) -> int:
+    """(query, key) pairs of one head of a sequence of n tokens under the causal mask and the
+    window (left, right) (negative: no limit): query i sees keys max(0, i - left) ..
+    min(n - 1, i + right, i if causal)."""
+    total = 0
+    for i in range(n):
+        hi = n - 1
+        if causal:
+            hi = min(hi, i)
+        if right >= 0:
+            hi = min(hi, i + right)
+        lo = max(0, i - left) if left >= 0 else 0
+        total += max(0, hi - lo + 1)
+    return total
 
 
 def progress(msg: str) -> None:
@@ -350,6 +368,25 @@ def main():
         from exact_attention_06_amd.workloads import DECODE_WORKLOADS
         for name in ("decode_b16_hq32_hkv8_nk8k_d128", "decode_b2_h32_nk32k_d128"):
             extra[name] = decode_case(DECODE_WORKLOADS[name], args.steps, args.warmup, 100.0)
+        from exact_attention_06_amd import fa_fwd_ext
+        from exact_attention_06_amd.workloads import EXT_WORKLOADS, make_ext_inputs
+        for name in ("gqa_b2_hq16_hkv4_n8k_d128_causal", "swa_b2_hq16_hkv4_n8k_d128_w4096",
+                     "varlen_16docs_hq16_hkv4_n16k_d128"):
+            we = EXT_WORKLOADS[name]
+            q, k, v, cu = make_ext_inputs(we)
+            lens = [we.N] * we.B if cu is None else [int(x) for x in (cu[1:] - cu[:-1])]
+            pairs = sum(visible_pairs(n, we.causal, we.window[0], we.window[1]) for n in lens)
+            fl = 4.0 * we.d * we.Hq * pairs
+            q, k, v = q.cuda(), k.cuda(), v.cuda()
+            cud = None if cu is None else cu.cuda()
+            mx = we.N if cu is None else max(lens)
+            o = torch.empty_like(q)
+            lse = torch.empty((we.B, we.Hq, we.N), dtype=torch.float32, device="cuda")
+            m = time_launches(torch, lambda: fa_fwd_ext(q, k, v, o, lse, causal=we.causal, window=we.window,
+                                                        cu_seqlens=cud, max_seqlen=mx), s2, w2, 100.0)
+            extra[name] = {"ms": round(m, 4), "TFLOP/s": round(fl / m / 1e9, 1), "visible_pairs_per_head": pairs}
+            progress(f"{name}: {m:.3f} ms, {fl / m / 1e9:.1f} TFLOP/s")
+            del q, k, v, o, lse
         result["extra"] = extra
     # calibration GEMM (hipBLASLt via torch): what a plain bf16 GEMM sustains on this GPU now
     a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")

@@ -23,7 +23,7 @@ STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_ALIGN", -3: "FA_ERR_SHAPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
 }
-EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_decode_workspace_size", "fa_decode",
+EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_ext", "fa_decode_workspace_size", "fa_decode",
             "fa_status_string", "fa_version")
 
 _lib = None
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_fp8.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     L.fa_bwd.restype = i
+    L.fa_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, i, i, vp]
+    L.fa_fwd_ext.restype = i
     L.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
@@ -220,4 +222,40 @@ def fa_decode(q, k, v, o=None, lse=None, workspace=None, *, scale=None, causal=F
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
                            int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(stream)))
+    return o, lse
+
+
+def fa_fwd_ext(q, k, v, o=None, lse=None, *, scale=None, causal=False, window=(-1, -1), cu_seqlens=None,
+               max_seqlen=None, want_lse=True, stream=None):
+    """Attention forward with grouped key/value heads, a sliding window (left, right) (a
+    negative bound: no limit) and packed variable-length sequences.
+
+    Without cu_seqlens: q [B, Hq, N, d], k, v [B, Hkv, N, d] (bfloat16, Hkv divides Hq). With
+    cu_seqlens (int32 GPU tensor of B + 1 offsets from 0 to N): q [1, Hq, N, d], k, v
+    [1, Hkv, N, d]; max_seqlen is the longest sequence (read back from cu_seqlens, which
+    synchronises, when not given). Returns (o, lse) shaped like q and [batch, Hq, N]."""
+    Bq, Hq, N, d = _bhnd(q)
+    Bk, Hkv, Nk, dk = _bhnd(k)
+    if tuple(v.shape) != tuple(k.shape) or Bk != Bq or Nk != N or dk != d:
+        raise ValueError("k and v must be [B, Hkv, N, d] with the batch, length and head dim of q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("fa_fwd_ext takes bfloat16 tensors")
+    if cu_seqlens is not None:
+        if Bq != 1:
+            raise ValueError("packed sequences: the batch dimension must be 1")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets")
+        B = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if B > 0 else 0
+    else:
+        B, max_seqlen = Bq, 0
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((Bq, Hq, N), dtype=torch.float32, device=q.device)
+    _require_gpu(q, k, v, o, lse, cu_seqlens)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, scale,
+                            int(bool(causal)), int(window[0]), int(window[1]), _ptr(cu_seqlens), int(max_seqlen),
+                            FA_BF16, _stream(stream)))
     return o, lse

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;   // 0.3.0: fa_decode
+constexpr int kVersion = 400;   // 0.4.0: fa_fwd_ext
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -60,6 +60,28 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == FA_BF16) return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s));
     return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s));
+}
+
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+               int d, float scale, int causal, int window_left, int window_right, const int* cu_seqlens,
+               int max_seqlen, int dtype, void* stream) {
+    if (B < 0 || Hkv < 1 || Hq < 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    const int nb = cu_seqlens != nullptr ? 1 : B;   // batch dimension of the tensors
+    int st = check_common(nb, Hq, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (cu_seqlens != nullptr && (max_seqlen < 0 || max_seqlen > N)) return FA_ERR_SHAPE;
+    const int rows_n = cu_seqlens != nullptr ? max_seqlen : N;
+    // workgroups: B Hq rows of ceil(rows_n / 128) query blocks
+    if ((long long)B * Hq * ((rows_n + 127) / 128) > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)B * Hq * rows_n == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return FA_ERR_ALIGN;
+    return from_hip(fa::launch_fwd_ext_bf16(q, k, v, o, lse, B, Hq, Hkv, N, max_seqlen, d, scale, causal != 0,
+                                            window_left, window_right, cu_seqlens, static_cast<hipStream_t>(stream)));
 }
 
 int fa_prep_fp8(const float* x, void* x8, float* sc, const float* signs, int B, int H, int N, int d, void* stream) {

@@ -41,7 +41,31 @@ hipError_t dispatch(const void* q, const void* k, const void* v, void* o, float*
                                                                           BH, N, scale, stream);
 }
 
+template <int D, int BC, int NQ, int MINB>
+hipError_t dispatch_ext(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Ngrid,
+                        float scale, bool causal, const FwdExt& ext, hipStream_t stream) {
+    constexpr InKind K = InKind::BF16;
+    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, true, 4, true>(q, k, v, nullptr, nullptr, nullptr, o,
+                                                                                 lse, BH, Ngrid, scale, stream, ext)
+                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, true, 4, true>(q, k, v, nullptr, nullptr, nullptr, o,
+                                                                                  lse, BH, Ngrid, scale, stream, ext);
+}
+
 }  // namespace
+
+// grouped heads / sliding window / packed sequences: the 4-wave tiles of the plain kernel
+hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int N, int max_seqlen, int d, float scale, bool causal, int left, int right,
+                               const int* cu_seqlens, hipStream_t stream) {
+    const FwdExt ext{Hq, Hq / Hkv, left < 0 ? -1 : left, right < 0 ? -1 : right, N, cu_seqlens};
+    const int BH = B * Hq;
+    const int Ngrid = cu_seqlens != nullptr ? max_seqlen : N;
+    switch (d) {
+        case 64: return dispatch_ext<64, 64, 1, 2>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
+        case 128: return dispatch_ext<128, FA_D128_BC, 1, FA_D128_MINB>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream) {

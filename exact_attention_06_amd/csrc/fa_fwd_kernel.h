@@ -98,16 +98,30 @@ struct QOperand<InKind::FP8> { typedef i32x8 type; };
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// Extended problems (EXT kernels): grouped key/value heads, a sliding window and packed
+// variable-length sequences. A workgroup's (batch or sequence, head) index is seq Hq + h; query
+// head h reads key/value head h / g. Window: query i sees key j iff i - left <= j <= i + right
+// (a negative bound: no limit; the causal mask sets right = 0). With cu (cu[s], cu[s+1] the
+// token range of sequence s; the batch dimension is then 1) positions count from the start of
+// the sequence and keys of other sequences are never visited. ntot: tokens per (batch, head)
+// row of the tensors (N, or the total of the packed sequences).
+struct FwdExt {
+    int Hq, g, left, right, ntot;
+    const int* cu;
+};
+
 // WAVES: waves per workgroup (each owns 32 NQ queries; all share the K/V tiles).
 // NQ: 32-query tiles per wave (the workgroup owns WAVES * 32 * NQ queries). With NQ = 2 every K
 // and V^T operand read from LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
 // PIPE: compute the scores of block j+1 while the softmax of block j runs (needs registers
 // for two score tiles); without it each block's scores are computed just before its softmax.
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES>
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES, bool EXT = false>
 __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    bf16_t* __restrict__ O, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */) {
+    bf16_t* __restrict__ O, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */,
+    FwdExt ext) {
+    static_assert(!(EXT && KIND == InKind::FP8), "extended problems take bf16 inputs");
     constexpr int NT = 64 * WAVES;    // threads per workgroup
     using C = FwdCfg<KIND, D, BC, NT>;
     using QT = typename QOperand<KIND>::type;
@@ -138,10 +152,25 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 #pragma unroll
     for (int n = 0; n < NQ; ++n) qrow[n] = q0w + 32 * n + col;
 
-    const size_t head_off = (size_t)bh * N * D;   // elements
+    // rows of this head (sequence) and the row index of its row 0 in Q / O / LSE and in K / V
+    size_t qbase = (size_t)bh * N, kvbase = (size_t)bh * N;
+    if constexpr (EXT) {
+        const int seq = bh / ext.Hq;
+        const int hq = bh - seq * ext.Hq;
+        int start = 0;
+        if (ext.cu != nullptr) {   // offsets clamped to [0, ntot]: never a read outside the tensors
+            start = min(max(ext.cu[seq], 0), ext.ntot);
+            N = min(max(ext.cu[seq + 1], start), ext.ntot) - start;
+        }
+        const int bb = ext.cu != nullptr ? 0 : seq;
+        qbase = ((size_t)bb * ext.Hq + hq) * ext.ntot + start;
+        kvbase = ((size_t)bb * (ext.Hq / ext.g) + hq / ext.g) * ext.ntot + start;
+        if (q0 >= N) return;   // the grid covers the longest sequence (uniform per workgroup)
+    }
+    const size_t head_off = qbase * D;   // elements
     const uint8_t* Qh = (const uint8_t*)Qv + head_off * C::IN_BYTES;
-    const uint8_t* Kh = (const uint8_t*)Kv + head_off * C::IN_BYTES;
-    const uint8_t* Vh = (const uint8_t*)Vv + head_off * C::IN_BYTES;
+    const uint8_t* Kh = (const uint8_t*)Kv + kvbase * D * C::IN_BYTES;
+    const uint8_t* Vh = (const uint8_t*)Vv + kvbase * D * C::IN_BYTES;
     // buffer resources over this head's K and V: reads past row N return zero
     const __amdgpu_buffer_rsrc_t rK =
         __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * C::ROW_BYTES, kBufferConfig);
@@ -151,6 +180,18 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const int nkb_all = (N + BC - 1) / BC;
     int nkb = nkb_all;
     if (CAUSAL) nkb = min(nkb_all, (min(q0 + BR, N) - 1) / BC + 1);
+    // EXT: key blocks [jlo, nkb) reach the window of some query of the workgroup; blocks
+    // below jfree reach below some query's window (masked)
+    int jlo = 0, jfree = 0;
+    const int right = CAUSAL ? 0 : (EXT ? ext.right : -1);
+    if constexpr (EXT) {
+        const int qlast = min(q0 + BR, N) - 1;
+        if (right >= 0) nkb = min(nkb_all, (qlast + right) / BC + 1);
+        if (ext.left >= 0) {
+            jlo = max(0, q0 - ext.left) / BC;
+            jfree = max(0, qlast - ext.left + BC - 1) / BC;
+        }
+    }
 
     // score scale (log2 units); FP8 adds the Q block scale of each query tile
     float cq[NQ];
@@ -344,20 +385,24 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     auto mask = [&](f32x16 (*st)[NQ], int kb) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
-            const int lim = (CAUSAL ? min(qrow[n], N - 1) : N - 1) - kb - key8h;
+            const int lim = (right >= 0 ? min(qrow[n] + right, N - 1) : N - 1) - kb - key8h;
+            // EXT window: keys before qrow - left are hidden too
+            const int low = (EXT && ext.left >= 0) ? qrow[n] - ext.left - kb - key8h : -(1 << 30);
 #pragma unroll
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int off = 32 * t + 16 * ((i >> 2) >> 1) + 4 * ((i >> 2) & 1) + (i & 3);
-                    st[t][n][i] = off > lim ? -INFINITY : st[t][n][i];
+                    if constexpr (EXT) st[t][n][i] = (off > lim || off < low) ? -INFINITY : st[t][n][i];
+                    else st[t][n][i] = off > lim ? -INFINITY : st[t][n][i];
                 }
         }
     };
-    // blocks [0, nfull) need no mask for any query of the workgroup
+    // blocks [jfree, nfull) need no mask for any query of the workgroup
     int nfull;
-    if (CAUSAL) nfull = min(N / BC, (q0 + 1) / BC);
+    if (right >= 0) nfull = min(N / BC, (q0 + right + 1) / BC);
     else nfull = N / BC;
+    auto needmask = [&](int x) { return x >= nfull || (EXT && x < jfree); };
     auto kscale = [&](int jj) {
         if constexpr (C::F8) return SK[(size_t)bh * nsb + jj * BC / 64];
         return 1.f;
@@ -401,7 +446,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         if (NEXT) load_v(kb + BC, smV[B ^ 1]);
         if constexpr (!PIPE) {
             qk(smK[B], s_cur);
-            if (j >= nfull) mask(s_cur, kb);
+            if (needmask(j)) mask(s_cur, kb);
             row_max(s_cur, j);
         }
         // ---- rescale the accumulators for block j's reference max (rare with TAU > 0)
@@ -474,33 +519,43 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         __syncthreads();
     };
 
-    // ---- prologue: K_0, V_0 (and K_1, the scores and row max of block 0 with the pipeline)
-    load_k(0, smK[0]);
-    load_v(0, smV[0]);
-    if (PIPE && nkb > 1) load_k(BC, smK[1]);
+    // ---- prologue: K_jlo, V_jlo (and K_jlo+1, the scores and row max of block jlo with the
+    // pipeline); jlo = 0 except for windows
+    const int kb0 = jlo * BC;
+    load_k(kb0, smK[0]);
+    load_v(kb0, smV[0]);
+    if (PIPE && nkb > jlo + 1) load_k(kb0 + BC, smK[1]);
     __builtin_amdgcn_s_waitcnt(0);
     store_v(smV[0]);
     __syncthreads();
     if constexpr (PIPE) {
         qk(smK[0], s_buf[0]);
-        if (nfull == 0) mask(s_buf[0], 0);
-        row_max(s_buf[0], 0);
+        if (needmask(jlo)) mask(s_buf[0], kb0);
+        row_max(s_buf[0], jlo);
         __syncthreads();   // every wave is done with smK[0] before block 0 refills it
     }
 
-    // blocks in pairs (even j in buffer 0); block j+1's mask is needed iff j + 1 >= nfull
-    int j = 0;
+    // blocks in pairs (block jlo + even in buffer 0); block j+1's mask is needed iff
+    // j + 1 >= nfull (or, for windows, j + 1 < jfree)
+    int j = jlo;
+    if constexpr (EXT) {
+        // the window's lower edge: the next block reaches below some query's window
+        for (; j + 2 < nkb && j + 1 < jfree; j += 2) {
+            step(j, IC<0>{}, IC<1>{}, IC<1>{});
+            step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
+        }
+    }
     for (; j + 2 < nkb && j + 2 < nfull; j += 2) {
         step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<1>{}, IC<0>{});
     }
     for (; j + 2 < nkb; j += 2) {
-        if (j + 1 >= nfull) step(j, IC<0>{}, IC<1>{}, IC<1>{});
+        if (needmask(j + 1)) step(j, IC<0>{}, IC<1>{}, IC<1>{});
         else step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
     }
     if (j + 1 < nkb) {
-        if (j + 1 >= nfull) step(j, IC<0>{}, IC<1>{}, IC<1>{});
+        if (needmask(j + 1)) step(j, IC<0>{}, IC<1>{}, IC<1>{});
         else step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<0>{}, IC<0>{});
     } else {
@@ -543,7 +598,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                         *(bf16x4*)(stg + col * OROW + 16 * ((4 * e + a) ^ (col & OSW)) + 8 * h) = ov;
                     }
                 if (LSE != nullptr && h == 0 && qrow[n] < N)
-                    LSE[(size_t)bh * N + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                    LSE[qbase + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
                 // the wave reads back what its other lanes wrote
                 __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
                 __builtin_amdgcn_wave_barrier();
@@ -563,16 +618,19 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     }
 }
 
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES = 4>
+// EXT kernels: BH = (sequences or batches) x Hq workgroup rows, N = the longest sequence (the
+// grid's query blocks), ext as described at FwdExt
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES = 4, bool EXT = false>
 hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const float* sq, const float* sk,
-                             const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream) {
+                             const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream,
+                             FwdExt ext = FwdExt{}) {
     constexpr int BR = WAVES * 32 * NQ;
     const int numQB = (N + BR - 1) / BR;
     const int nsb = (N + 63) / 64;
     const long long total = (long long)BH * numQB;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES>), dim3((unsigned)total), dim3(64 * WAVES),
-                       0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e);
+    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT>), dim3((unsigned)total),
+                       dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e, ext);
     return hipGetLastError();
 }
 

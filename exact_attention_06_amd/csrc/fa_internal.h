@@ -11,6 +11,14 @@ namespace fa {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream);
 
+// Grouped heads, sliding window, packed sequences (bf16, d in {64, 128}). Without cu_seqlens:
+// q, o [B, Hq, N, d], k, v [B, Hkv, N, d], lse [B, Hq, N]. With cu_seqlens (device int32, B + 1
+// offsets into N tokens): q, o [Hq, N, d], k, v [Hkv, N, d], lse [Hq, N], every sequence at most
+// max_seqlen long. left / right < 0: no limit on that side.
+hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int N, int max_seqlen, int d, float scale, bool causal, int left, int right,
+                               const int* cu_seqlens, hipStream_t stream);
+
 // fp32 Q, K, V, O [BH, N, d]; lse [BH, N] or null. d in {64, 128, 256}.
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           float scale, bool causal, hipStream_t stream);

@@ -18,6 +18,10 @@ below have the shapes, sizes and value distributions of the benchmark cases):
   generator (after Q, K, V), cast to bfloat16.
 - Decoding workloads: Q [B, Hq, Nq, d], then K and V [B, Hkv, Nk, d] (the key/value cache),
   iid N(0, 1) from one seeded generator in that order, cast to bfloat16.
+- Grouped-head / window / packed workloads: Q [B, Hq, N, d], then K and V [B, Hkv, N, d], iid
+  N(0, 1), bfloat16; packed sequence lengths are either given (the pages' example of three
+  documents of 300, 1000 and 748 tokens) or cut from the same generator after V: the N
+  tokens are split at nseq - 1 distinct positions drawn by torch.randperm(N - 1) + 1.
 - The softmax scale is 1/sqrt(d) throughout.
 
 Layout is [B, H, N, d], contiguous.
@@ -121,6 +125,62 @@ def make_decode_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed
     k = torch.randn(B, Hkv, Nk, d, dtype=torch.float32, generator=g)
     v = torch.randn(B, Hkv, Nk, d, dtype=torch.float32, generator=g)
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@dataclass(frozen=True)
+class ExtWorkload:
+    """Forward with grouped key/value heads, an optional window (left, right) and optional packed
+    sequences (lengths given, or nseq > 0 seeded cuts of N tokens; the batch is then 1)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    window: tuple
+    seed: int
+    lengths: tuple = ()
+    nseq: int = 0
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def packed(self) -> bool:
+        return bool(self.lengths) or self.nseq > 0
+
+
+EXT_WORKLOADS = {
+    w.name: w
+    for w in [
+        ExtWorkload("gqa_b2_hq16_hkv4_n8k_d128_causal", 2, 16, 4, 8192, 128, True, (-1, -1), 12,
+                    note="grouped heads (16 query heads share 4 key/value heads), causal: the pages' flash_attn example"),
+        ExtWorkload("swa_b2_hq16_hkv4_n8k_d128_w4096", 2, 16, 4, 8192, 128, True, (4095, 0), 13,
+                    note="the same with the sliding window (4095, 0): 4096 keys including the query"),
+        ExtWorkload("varlen_3docs_hq16_hkv4_d128", 1, 16, 4, 2048, 128, True, (-1, -1), 14, lengths=(300, 1000, 748),
+                    note="the pages' packed row: three documents of 300, 1000, 748 tokens, causal"),
+        ExtWorkload("varlen_16docs_hq16_hkv4_n16k_d128", 1, 16, 4, 16384, 128, True, (-1, -1), 15, nseq=16,
+                    note="16 packed documents of seeded lengths in 16384 tokens, causal"),
+    ]
+}
+
+
+def make_ext_inputs(w: ExtWorkload):
+    """(q, k, v, cu_seqlens or None) for an ExtWorkload; cu_seqlens is an int32 CPU tensor."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = torch.randn(w.B, w.Hq, w.N, w.d, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    k = torch.randn(w.B, w.Hkv, w.N, w.d, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    v = torch.randn(w.B, w.Hkv, w.N, w.d, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    cu = None
+    if w.lengths:
+        cu = torch.tensor([0] + list(torch.tensor(w.lengths).cumsum(0).tolist()), dtype=torch.int32)
+    elif w.nseq > 0:
+        cuts = torch.sort(torch.randperm(w.N - 1, generator=g)[: w.nseq - 1] + 1).values
+        cu = torch.cat([torch.zeros(1, dtype=torch.int64), cuts, torch.tensor([w.N])]).to(torch.int32)
+    return q, k, v, cu
 
 
 OUTLIER_FRACTION = 0.001

@@ -153,6 +153,39 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_ext - the attention forward with grouped key/value heads, a sliding window and
+ * packed variable-length sequences (any combination).
+ *
+ * Sources: the flash_attn interface example and its packed-batch example on "Learn: The
+ * Memory Wall & FlashAttention"; Exercise 5 of "FlashAttention 2 & 3: Work Partitioning,
+ * Warp Specialization & FP8" (sliding window with key blocks outside the window skipped
+ * and the partial blocks masked).
+ *
+ * - Grouped heads: Hkv divides Hq; query head h reads key/value head h / (Hq / Hkv).
+ * - Window: query i sees key j iff i - window_left <= j <= i + window_right; a negative
+ *   bound means no limit on that side. With causal = 1 keys after the query are hidden
+ *   as well (window_right is then irrelevant): (4095, 0) with causal is a window of
+ *   4096 keys including the query. Key blocks outside every query's window are skipped.
+ * - Packed sequences: with cu_seqlens == NULL the tensors are q, o [B, Hq, N, d],
+ *   k, v [B, Hkv, N, d], lse [B, Hq, N] (bfloat16; lse fp32, optional). With cu_seqlens
+ *   (device int32 [B + 1], 4-byte aligned: B sequences, sequence s is tokens
+ *   cu_seqlens[s] .. cu_seqlens[s+1]-1, cu_seqlens[0] = 0, cu_seqlens[B] = N) the batch
+ *   dimension is 1: q, o [Hq, N, d], k, v [Hkv, N, d], lse [Hq, N]; a query sees keys of
+ *   its own sequence only, and window and causal positions count from the sequence start.
+ *   max_seqlen (<= N) must be at least the longest sequence: rows beyond it are not
+ *   written. The offsets are read on the GPU and clamped to [0, N]; offsets that
+ *   decrease or exceed N give undefined outputs but no access outside the tensors.
+ *   Tokens not covered by any sequence are not written.
+ *
+ *   d 64 or 128 (FA_ERR_HEADDIM); dtype FA_BF16 only (FA_ERR_DTYPE); Hkv < 1 or not a
+ *   divisor of Hq, or max_seqlen outside [0, N] with cu_seqlens: FA_ERR_SHAPE.
+ */
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+               int window_left, int window_right, const int* cu_seqlens, int max_seqlen,
+               int dtype, void* stream);
+
+/*
  * fa_decode - attention of a few query positions against a long key/value
  * sequence (autoregressive decoding), split over the keys.
  *

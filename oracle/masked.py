@@ -86,6 +86,21 @@ def attention_ext_fp64(q, k, v, scale: float, causal: bool, window=(-1, -1), cu_
     return out, lse
 
 
+def attention_ext_rows_fp64(q, k, v, scale: float, causal: bool, window, b: int, h: int, rows):
+    """(O[rows], LSE[rows]) of batch b, query head h, without packing: the same three passes
+    restricted to the chosen query rows (a rows x N block of scores), for long sequences."""
+    g = q.shape[1] // k.shape[1]
+    qh, kh, vh = (_as_f64(x) for x in (q[b, h], k[b, h // g], v[b, h // g]))
+    n = qh.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    ok = visible_mask(n, causal, int(window[0]), int(window[1]))[rows]
+    s = np.where(ok, scale * (qh[rows] @ kh.T), -np.inf)
+    m = s.max(axis=1)                           # every row sees itself: finite
+    e = np.where(ok, np.exp(s - m[:, None]), 0.0)
+    l = e.sum(axis=1)
+    return (e / l[:, None]) @ vh, m + np.log(l)
+
+
 def visible_pairs(n: int, causal: bool, left: int, right: int) -> int:
     """Number of (query, key) pairs one head of one sequence of length n computes with."""
     i = np.arange(n)

@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_decode_workspace_size",
-                                           "fa_decode", "fa_status_string", "fa_version"])
+    assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_ext",
+                                           "fa_decode_workspace_size", "fa_decode", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_version_and_status_strings(L):
     from exact_attention_06_amd import _lib
 
-    assert L.fa_version() == 300
+    assert L.fa_version() == 400
     for code, name in _lib.STATUS_NAMES.items():
         s = _lib.status_string(code)
         assert s and s != "unknown status", name
@@ -167,3 +167,30 @@ def test_decode_argument_errors(L):
     p[5] = None
     assert dec(L, p) == -1                # the workspace is required when its size is > 0
     assert dec(L, [None] * 6, Nq=0) == 0  # empty: nothing touched, nothing launched
+
+
+def ext(L, ptrs=None, B=2, Hq=8, Hkv=2, N=256, d=128, scale=0.088, causal=1, left=-1, right=-1, cu=None,
+        max_seqlen=0, dtype=1):
+    p = [P] * 5 if ptrs is None else ptrs
+    return L.fa_fwd_ext(*p, B, Hq, Hkv, N, d, scale, causal, left, right, cu, max_seqlen, dtype, None)
+
+
+def test_fwd_ext_argument_errors(L):
+    assert ext(L, d=256) == -4            # 64 and 128
+    assert ext(L, dtype=0) == -5          # bfloat16 only
+    assert ext(L, scale=-1.0) == -6
+    assert ext(L, causal=7) == -8
+    assert ext(L, Hkv=3) == -3            # Hkv must divide Hq
+    assert ext(L, Hkv=0) == -3
+    assert ext(L, N=-5) == -3
+    assert ext(L, cu=P, max_seqlen=257) == -3    # longer than N
+    assert ext(L, cu=P, max_seqlen=-1) == -3
+    assert ext(L, cu=P + 2, max_seqlen=100) == -2  # int32 offsets: 4-byte aligned
+    for i in range(4):                    # q k v o
+        p = [P] * 5
+        p[i] = None
+        assert ext(L, p) == -1, i
+        p[i] = P + 8
+        assert ext(L, p) == -2, i
+    assert ext(L, [None] * 5, N=0) == 0                      # empty: nothing launched
+    assert ext(L, [None] * 5, cu=P, max_seqlen=0) == 0       # packed, every sequence empty

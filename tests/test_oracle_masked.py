@@ -11,7 +11,8 @@
   keys and values of one sequence leaves the others unchanged (no attention across the
   boundaries); empty sequences are allowed;
 - grouped heads equal the key/value heads repeated Hq / Hkv times;
-- the visible-pair count equals the number of True entries of the mask.
+- the visible-pair count equals the number of True entries of the mask;
+- the sampled-rows form equals the full form on those rows.
 """
 
 import math
@@ -21,7 +22,7 @@ import pytest
 import torch
 
 from oracle.attention import attention_fp64
-from oracle.masked import attention_ext_fp64, visible_mask, visible_pairs
+from oracle.masked import attention_ext_fp64, attention_ext_rows_fp64, visible_mask, visible_pairs
 
 
 def _rand(seed, *shape):
@@ -123,3 +124,13 @@ def test_grouped_heads_equal_repeated_heads(window):
                                                  (50, False, 4, 6), (7, False, 0, 0), (64, True, 100, -1)])
 def test_visible_pairs(n, causal, left, right):
     assert visible_pairs(n, causal, left, right) == int(visible_mask(n, causal, left, right).sum())
+
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (20, 0)), (False, (7, 12)), (False, (-1, -1))])
+def test_sampled_rows_equal_full(causal, window):
+    q = _rand(25, 2, 4, 70, 8)
+    k, v = _rand(26, 2, 2, 70, 8), _rand(27, 2, 2, 70, 8)
+    o, lse = attention_ext_fp64(q, k, v, 0.3, causal, window)
+    rows = [0, 5, 31, 32, 69]
+    o2, lse2 = attention_ext_rows_fp64(q, k, v, 0.3, causal, window, 1, 3, rows)
+    assert np.allclose(o2, o[1, 3, rows], rtol=0, atol=1e-13) and np.allclose(lse2, lse[1, 3, rows], rtol=0, atol=1e-13)
