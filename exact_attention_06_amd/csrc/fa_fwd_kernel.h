@@ -142,9 +142,19 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const int h = lane >> 5;        // lane half
     const int col = lane & 31;      // query column owned by this lane in each query tile
 
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = w / numQB;
-    const int qi = w - bh * numQB;
+    int bh, qi;
+    if (EXT && ext.cu != nullptr) {
+        // packed sequences of unequal lengths: query-block index major, so that the costliest
+        // blocks of every sequence and head are dispatched first and spread over all XCDs (the
+        // contiguous per-XCD ranges of the remap would put a long sequence on one or two XCDs)
+        const int rows = gridDim.x / numQB;
+        qi = blockIdx.x / rows;
+        bh = blockIdx.x - qi * rows;
+    } else {
+        const int w = xcd_remap(blockIdx.x, gridDim.x);
+        bh = w / numQB;
+        qi = w - bh * numQB;
+    }
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
     const int q0w = q0 + wave * 32 * NQ;
