@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV with wave pairs (d = 128)
+// dK, dV with wave pairs
 // ------------------------------------------------------------------------------------------
 // One 128-key block per workgroup of 8 waves; waves p and p + 4 share the keys k0 + 32p .. +31.
 // Wave p (the P wave) keeps K resident; in step i it adds dV^T += dO^T P of block i - 1, then
@@ -387,8 +387,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
     constexpr int W = 8;
     constexpr int BQ = 32, BK = 128;
-    using C = TileCfg<D, BQ, W>;
+    // a 32-row tile is TB / 1 KB load regions: 8 at d = 128 (every wave loads a region of both
+    // the Q and the dO tile), 4 at d = 64 (the P waves load the Q tile, the dS waves the dO tile)
+    constexpr int LW = TileCfg<D, BQ, 1>::TB / 1024 >= W ? W : W / 2;
+    using C = TileCfg<D, BQ, LW>;
     constexpr int TB = C::TB;          // one 32-row tile
+    static_assert(C::LOADS == 1, "one load region per wave and tile");
     constexpr int PT = 64 * 16 * 4;    // one P tile: 16 fp32 per lane, stored as 4 planes of 16 B per lane
     constexpr int OQ = 0, OD = 3 * TB, OP = 6 * TB;
     constexpr int LDS_BYTES = OP + 12 * PT;
@@ -413,8 +417,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, N * C::ROW, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc((void*)(NL2 + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rDl = __builtin_amdgcn_make_buffer_rsrc((void*)(Dl + (size_t)bh * N), (short)0, N * 4, kBufferConfig);
-    TileAddr<D, BQ, W> ta;
-    ta.init(wave, lane);
+    TileAddr<D, BQ, LW> ta;
+    const int lwave = LW == W ? wave : (wave & 3);   // this wave's load region
+    ta.init(lwave, lane);
 
     bf16x8 kv[C::KSTEPS];   // K (P wave) or V (dS wave) of the pair's 32 keys
     load_resident<D>(kv, (pwave ? K : V) + head, krow, N, h);
@@ -432,8 +437,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     uint8_t* const pbuf = sm + OP + 3 * PT * pair;
     auto slot = [&](int i) __attribute__((always_inline)) { return ((i - u) % 3 + 3) % 3; };
     auto load_tiles = [&](int i, int t) __attribute__((always_inline)) {
-        ta.load(rQ, sm + OQ + TB * t, i * BQ, wave);
-        ta.load(rO, sm + OD + TB * t, i * BQ, wave);
+        if (LW == W || pwave) ta.load(rQ, sm + OQ + TB * t, i * BQ, lwave);
+        if (LW == W || !pwave) ta.load(rO, sm + OD + TB * t, i * BQ, lwave);
     };
     // four values per lane from a per-query fp32 vector: registers 4v .. 4v+3 of tile rows
     // q0 + 16(v/2) + 8h + 4(v%2) + 0..3
@@ -566,7 +571,11 @@ void launch_dkdv(const bf16_t* Qb, const bf16_t* Kb, const bf16_t* Vb, const bf1
     constexpr int kind = D > 64 ? 2 : 0;
 #elif defined(FA_BWD_FUSED_DKDV)
     constexpr int kind = 0;
+#elif defined(FA_BWD_PAIR_D64)
+    constexpr int kind = 1;
 #else
+    // d = 64: the fused kernel (a pair's 8 products per step are too few to pay for the
+    // per-step barrier of 8 waves and the P exchange: 2.89 vs 2.22 ms at B=8 H=16 N=4k)
     constexpr int kind = D > 64 ? 1 : 0;
 #endif
     if constexpr (kind == 1) {
