@@ -30,7 +30,9 @@ causal), the same count for every backend. Also reported:
 rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
 ``--only-bwd`` times only the backward on the headline shape (for kernel traces
 of the backward kernels) and prints its own JSON line; ``--only-decode`` does the
-same for split-key decoding on the grouped-head 8K-cache workload.
+same for split-key decoding on the grouped-head 8K-cache workload, ``--only fp8``
+for the FP8 forward (inputs quantised once, untimed) and ``--only NAME`` for the
+bf16 or fp32 forward on the named workload (e.g. short_b64h16n512_d128).
 """
 
 from __future__ import annotations
@@ -63,6 +65,7 @@ def parse_args():
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--only-bwd", action="store_true")
     p.add_argument("--only-decode", action="store_true")
+    p.add_argument("--only", default=None, help="fp8, or a forward workload name")
     return p.parse_args()
 
 
@@ -260,6 +263,36 @@ def main():
                           "ms_per_step": r["ms"], "steps": args.steps,
                           "config": {"workload": f"fa_decode B={wd.B} Hq={wd.Hq} Hkv={wd.Hkv} Nq={wd.Nq} "
                                                  f"Nk={wd.Nk} d={wd.d} bf16"}}))
+        return 0
+
+    if args.only == "fp8":
+        wf = WORKLOADS["fp8_b4h16n8k_d128"]
+        q, k, v, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))
+        q8, sq = fa_prep_fp8(q, signs)
+        k8, sk = fa_prep_fp8(k, signs)
+        v8, sv = fa_prep_fp8(v)
+        del q, k, v
+        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device="cuda")
+        m = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), args.steps, args.warmup, 100.0)
+        print(json.dumps({"metric": "attention fwd TFLOP/s (4*B*H*N^2*d), e4m3 inputs", "value": round(wf.flops(False) / m / 1e9, 1),
+                          "unit": "TFLOP/s", "ms_per_step": round(m, 4), "steps": args.steps,
+                          "config": {"workload": f"fa_fwd_fp8 B={wf.B} H={wf.H} N={wf.N} d={wf.d} non-causal"}}))
+        return 0
+    if args.only is not None:
+        if args.only not in WORKLOADS or WORKLOADS[args.only].dtype == "fp8":
+            print(f"--only: fp8 or one of {sorted(n for n, x in WORKLOADS.items() if x.dtype != 'fp8')}", file=sys.stderr)
+            return 2
+        wx = WORKLOADS[args.only]
+        causal = wx.causal[0]
+        q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
+        o = torch.empty_like(q)
+        lse = torch.empty((wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
+        m = time_launches(torch, lambda: fa_fwd(q, k, v, o, lse, causal=causal), args.steps, args.warmup, 100.0)
+        nbytes = 4 * q.numel() * q.element_size() + lse.numel() * 4
+        print(json.dumps({"metric": "attention fwd", "TFLOP/s": round(wx.flops(causal) / m / 1e9, 2),
+                          "GB/s": round(nbytes / m / 1e6, 1), "ms_per_step": round(m, 4), "steps": args.steps,
+                          "bytes": nbytes, "config": {"workload": f"{wx.name} causal={causal}"}}))
         return 0
 
     if args.only_bwd:

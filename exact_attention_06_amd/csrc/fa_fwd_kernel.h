@@ -82,9 +82,19 @@ struct FwdCfg {
     static constexpr int VSWZ = VCPR - 1;
 };
 
-// swizzled 16-byte chunk position of chunk c in K row r / bf16 V row r
+// swizzled 16-byte chunk position of chunk c in K row r / bf16 V row r. An MFMA operand read
+// serves 16 lanes per cycle from the 64 banks (256 bytes) of LDS; those lanes read rows
+// swap_bits23(0..15) at one chunk position. Rows of 256 bytes or more: the XOR with
+// swap_bits23(r) puts the 16 rows on 16 different chunk positions. Shorter rows (e4m3 at
+// d = 128, bf16 at d = 64: 128 bytes; e4m3 at d = 64: 64 bytes) share a 256-byte bank line with
+// the RPB - 1 rows next to them, so rows that agree modulo RPB must differ in the XOR:
+// r / RPB, distinct over the 16 / RPB rows of each residue.
 template <int MASK>
-__device__ __forceinline__ int k_slot(int r, int c) { return c ^ (swap_bits23(r) & MASK); }
+__device__ __forceinline__ int k_slot(int r, int c) {
+    constexpr int RPB = 16 / (MASK + 1);   // rows per 256-byte bank line (MASK + 1 chunks per row)
+    if constexpr (RPB > 1) return c ^ ((r / RPB) & MASK);
+    return c ^ (swap_bits23(r) & MASK);
+}
 template <int MASK>
 __device__ __forceinline__ int v_slot(int r, int c) { return c ^ ((2 * (r & 3) ^ 8 * (r & 1)) & MASK); }
 
