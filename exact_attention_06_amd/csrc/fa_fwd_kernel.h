@@ -216,6 +216,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     // score scale (log2 units); FP8 adds the Q block scale of each query tile
     float cq[NQ];
     float svmax = 1.f;   // FP8: largest V block scale of this head
+    float l2svmax = 0.f;  // and its log2
 #pragma unroll
     for (int n = 0; n < NQ; ++n) cq[n] = c2;
     if constexpr (C::F8) {
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
         svmax = mx;
+        l2svmax = __log2f(mx);
     }
 
     // ---- Q^T operands (B of S^T = K Q^T): in tile n the lane holds query qrow[n]; step s
@@ -489,8 +491,10 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         float inv_r = 1.f;
         if constexpr (C::F8) {
             const float sv = SV[(size_t)bh * nsb + j * BC / 64];
-            lbias = __log2f(sv / svmax);
-            inv_r = svmax / sv;
+            // log2(s_V(j) / max s_V) and its inverse ratio without divisions (the block's P
+            // carries the ratio, the row sum divides it back out; both to within an ulp or two)
+            lbias = __log2f(sv) - l2svmax;
+            inv_r = svmax * __builtin_amdgcn_rcpf(sv);
         }
         const float ks = kscale(j);
         bf16x8 pf[NQ][C::CH];
