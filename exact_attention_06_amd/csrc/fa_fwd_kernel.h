@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     // that has seen no key yet has l = 0, and masked scores are -inf whatever the bias.
     constexpr float kNoMax = -1e30f;
     f32x16 acc[NQ][C::DT];
-    float m_run[NQ], l_run[NQ], alpha[NQ];
+    float m_run[NQ], l_run[NQ], m_blk[NQ];   // reference max, row sum, max of the next block
     bool grow[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         for (int e = 0; e < C::DT; ++e) acc[n][e] = f32x16{};
         m_run[n] = kNoMax;
         l_run[n] = 0.f;
-        alpha[n] = 1.f;
+        m_blk[n] = kNoMax;
         grow[n] = false;
     }
     // result register i = 4a + b of a 32-key tile holds key swap_bits23(8a + 4h + b)
@@ -429,7 +429,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         if constexpr (C::F8) return SK[(size_t)bh * nsb + jj * BC / 64];
         return 1.f;
     };
-    // row max of block jj: new reference max (moved only past 2^TAU), rescale factor
+    // row max of block jj (log2 units) and whether it moves the reference max, which happens
+    // only when it exceeds the reference by more than TAU (then it becomes the new reference)
     auto row_max = [&](f32x16 (*st)[NQ], int jj) {
         const float ks = kscale(jj);
 #pragma unroll
@@ -439,12 +440,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][n][i]);
-            mx = pair_max(mx) * (cq[n] * ks);
-            const float m_new = fmaxf(m_run[n], mx);
-            grow[n] = m_new > m_run[n] + tau;
-            const float m_ref = grow[n] ? m_new : m_run[n];
-            alpha[n] = fast_exp2(m_run[n] - m_ref);
-            m_run[n] = m_ref;
+            m_blk[n] = pair_max(mx) * (cq[n] * ks);
+            grow[n] = m_blk[n] > m_run[n] + tau;
         }
     };
 
@@ -471,20 +468,24 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             if (needmask(j)) mask(s_cur, kb);
             row_max(s_cur, j);
         }
-        // ---- rescale the accumulators for block j's reference max (rare with TAU > 0)
+        // ---- move the reference max to block j's max where it grew past TAU, rescaling the row
+        // sum and the accumulator by alpha = exp2(m_old - m_new) (rare with TAU > 0; elsewhere
+        // alpha would be exactly 1, so the whole update is skipped)
         bool any_grow = false;
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            l_run[n] *= alpha[n];
-            any_grow = any_grow || grow[n];
-        }
+        for (int n = 0; n < NQ; ++n) any_grow = any_grow || grow[n];
         if (wave_any(any_grow)) {
 #pragma unroll
-            for (int n = 0; n < NQ; ++n)
+            for (int n = 0; n < NQ; ++n) {
+                const float m_ref = grow[n] ? m_blk[n] : m_run[n];
+                const float alpha = fast_exp2(m_run[n] - m_ref);
+                m_run[n] = m_ref;
+                l_run[n] *= alpha;
 #pragma unroll
                 for (int e = 0; e < C::DT; ++e)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[n][e][i] *= alpha[n];
+                    for (int i = 0; i < 16; ++i) acc[n][e][i] *= alpha;
+            }
         }
         // ---- P_j = exp2(S_j ct - m) (FP8: times s_V(j) / max s_V)
         float lbias = 0.f;
