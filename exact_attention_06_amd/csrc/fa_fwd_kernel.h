@@ -502,14 +502,17 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
             const float ct = cq[n] * ks;
-            const float bias = lbias - m_run[n];
-            float lsum = 0.f;
+            // (-m, not 0 - m, for bf16: the negation then rides on the FMA as a modifier)
+            const float bias = C::F8 ? lbias - m_run[n] : -m_run[n];
+            float lsum;
 #pragma unroll
             for (int t = 0; t < C::MT; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float p = fast_exp2(__builtin_fmaf(s_cur[t][n][i], ct, bias));
-                    lsum += p;   // fp32 P: the logsumexp needs the unrounded sum
+                    // fp32 P: the logsumexp needs the unrounded sum (started at the first term,
+                    // not at 0, which would cost an add)
+                    lsum = (t == 0 && i == 0) ? p : lsum + p;
                     pf[n][2 * t + i / 8][i % 8] = (bf16_t)p;
                 }
             if constexpr (C::F8) lsum *= inv_r;
