@@ -8,8 +8,9 @@
 // key blocks so that dK and dV accumulate locally, and names fp32 atomics or a separate pass
 // for dQ; this file takes the separate pass (deterministic, no atomics):
 //
-// 1. bwd_delta_kernel: D = rowsum(dO o O) in fp32, one row per group of d/8 lanes, and the
-//    exp2 bias -LSE log2(e) of every row (both into the caller's workspace).
+// 1. bwd_delta_kernel: -D = -rowsum(dO o O) in fp32, one row per group of d/8 lanes, and the
+//    exp2 bias -LSE log2(e) of every row (both into the caller's workspace). The dP products
+//    start their accumulators from -D, so that they yield dP - D with no subtraction.
 // 2. bwd_dq_kernel, parallel over 128-query blocks (the forward's layout): each wave keeps
 //    Q^T and dO^T of its 32 queries in registers as MFMA B operands and streams 32-key blocks
 //    of K and V through LDS. S^T = K Q^T and dP^T = V dO^T put one query in each lane pair;
@@ -49,7 +50,7 @@ template <int D>
 constexpr int dkdv_rows() { return D <= 64 ? 32 : FA_DKDV_ROWS; }
 
 // ------------------------------------------------------------------------------------------
-// D = rowsum(dO o O)
+// -D = -rowsum(dO o O)
 // ------------------------------------------------------------------------------------------
 // also nl2 = -LSE log2(e), the exp2 bias of P = exp2(S c - LSE log2 e), read per query by the
 // dK / dV passes
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(const bf16_t* __
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (c == 0 && row < rows) {
-        delta[row] = acc;
+        delta[row] = -acc;
         nl2[row] = -LSE[row] * kLog2e;
     }
 }
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
     load_resident<D>(qf, Q + head, qrow, N, h);
     load_resident<D>(df, dO + head, qrow, N, h);
     const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
-    const float dlt = qrow < N ? Dl[(size_t)bh * N + qrow] : 0.f;
+    const float ndlt = qrow < N ? Dl[(size_t)bh * N + qrow] : 0.f;   // -D of this lane's query
 
     int nkb = (N + BC - 1) / BC;
     if (CAUSAL) nkb = min(nkb, (min(q0 + BR, N) - 1) / BC + 1);
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
             ta.load(rV, (B ? sV0 : sV1), kb + BC, wave);
         }
         // S^T = K Q^T and dP^T = V dO^T (keys x queries)
-        f32x16 st{}, dpt{};
+        // dP^T - D: the product starts from -D (the query's, in every register)
+        f32x16 st{}, dpt;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dpt[i] = ndlt;
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
             st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sK1 : sK0), s), qf[s], st, 0, 0, 0);
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
         for (int i = 0; i < 16; ++i) {
             float p = fast_exp2(__builtin_fmaf(st[i], c2, -lse2));
             if constexpr (MASK) p = (16 * (i / 8) + (i % 8)) > lim ? 0.f : p;
-            dsf[i / 8][i % 8] = (bf16_t)(p * (dpt[i] - dlt));
+            dsf[i / 8][i % 8] = (bf16_t)(p * dpt[i]);
         }
         // dQ^T += K^T dS^T
 #pragma unroll
@@ -305,7 +309,13 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 #pragma unroll
         for (int tt = 0; tt < QT; ++tt) {
             s[tt] = f32x16{};
-            dp[tt] = f32x16{};
+            // dP - D: the product starts from -D (register r of query tile tt: dq[tt][r / 4][r % 4])
+            if constexpr (DOK) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dp[tt][r] = dq[tt][r / 4][r % 4];
+            } else {
+                dp[tt] = f32x16{};
+            }
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
                 s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sQ1 : sQ0), st, tt), kf[st], s[tt], 0, 0, 0);
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
                     p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
                 }
                 if constexpr (DOV) pf[r / 8][r % 8] = (bf16_t)p;
-                if constexpr (DOK) dsf[r / 8][r % 8] = (bf16_t)(p * (dp[tt][r] - dq[tt][r / 4][r % 4]));
+                if constexpr (DOK) dsf[r / 8][r % 8] = (bf16_t)(p * dp[tt][r]);
             }
             // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries of tile tt
 #pragma unroll
@@ -509,8 +519,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         const int q0 = i * BQ;
         const uint8_t* tq = sm + OQ + TB * t;
         const uint8_t* td = sm + OD + TB * t;
-        f32x4 dl[4];   // D
+        f32x4 dl[4];   // -D, in the register layout of dP
         row_vals(rDl, q0, dl);
+        // dP, then dP - D (the -D loads are in flight while the product runs; starting the
+        // product from -D would make it wait for them)
         f32x16 dp{};
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
@@ -521,7 +533,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         for (int j = 0; j < 4; ++j) pv[j] = *(const f32x4*)(pb + 1024 * j);
         bf16x8 dsf[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsf[r / 8][r % 8] = (bf16_t)(pv[r / 4][r % 4] * (dp[r] - dl[r / 4][r % 4]));
+        for (int r = 0; r < 16; ++r) dsf[r / 8][r % 8] = (bf16_t)(pv[r / 4][r % 4] * (dp[r] + dl[r / 4][r % 4]));
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll

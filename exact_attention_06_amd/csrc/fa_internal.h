@@ -33,7 +33,7 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
                           hipStream_t stream);
 
 // bf16 backward: q, k, v, o, dout [BH, N, d], lse [BH, N] from the forward -> dq, dk, dv
-// [BH, N, d] bf16; delta [2, BH, N] fp32 workspace (D = rowsum(dO o O), then -LSE log2 e).
+// [BH, N, d] bf16; delta [2, BH, N] fp32 workspace (-D = -rowsum(dO o O), then -LSE log2 e).
 // d in {64, 128}.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,

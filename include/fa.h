@@ -143,7 +143,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  *   dout        [B, H, N, d] bfloat16, the gradient of the loss with respect to o.
  *   lse         [B, H, N] fp32, the forward's logsumexp (fa_fwd's lse).
  *   dq, dk, dv  [B, H, N, d] bfloat16 (outputs). Must not overlap the inputs.
- *   delta       [2, B, H, N] fp32 workspace owned by the caller (receives D, then
+ *   delta       [2, B, H, N] fp32 workspace owned by the caller (receives -D, then
  *               -LSE log2(e), the exponent bias the key-parallel passes read).
  *   d           64 or 128 (others: FA_ERR_HEADDIM).  dtype: FA_BF16 only
  *               (others: FA_ERR_DTYPE).  scale, causal: as in the forward call.
