@@ -140,10 +140,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = w / numQB;
-    const int qi = w - bh * numQB;
-    const int qb = CAUSAL ? (numQB - 1 - qi) : qi;   // heaviest blocks first
+    int bh, qi;   // causal: heaviest blocks first, across the XCD's heads
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL, bh, qi);
+    const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
     const int q0w = q0 + 32 * wave;
     const int qrow = q0w + col;
@@ -254,9 +253,8 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = w / numKB;
-    const int kbi = w - bh * numKB;   // causal: low key blocks see the most queries and come first
+    int bh, kbi;   // causal: low key blocks see the most queries and come first (across the XCD's heads)
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL, bh, kbi);
     const int k0 = kbi * BK;
     const int k0w = k0 + 32 * wave;
     const int krow = k0w + col;
@@ -426,9 +424,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const int pair = wave & 3;
     const bool pwave = wave < 4;
     const int h = lane >> 5, col = lane & 31;
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = w / numKB;
-    const int kbi = w - bh * numKB;   // causal: low key blocks see the most queries and come first
+    int bh, kbi;   // causal: low key blocks see the most queries and come first (across the XCD's heads)
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL, bh, kbi);
     const int k0 = kbi * BK;
     const int k0w = k0 + 32 * pair;
     const int krow = k0w + col;

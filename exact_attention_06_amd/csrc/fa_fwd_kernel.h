@@ -161,22 +161,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         qi = blockIdx.x / rows;
         bh = blockIdx.x - qi * rows;
     } else {
-        const int w = xcd_remap(blockIdx.x, gridDim.x);
-        bh = w / numQB;
-        qi = w - bh * numQB;
-        if (CAUSAL && (gridDim.x & 7) == 0) {
-            // each XCD walks its contiguous range of work items in order; ordering the range by
-            // query block first (across its heads) dispatches the costliest causal blocks of all
-            // of its heads before any lighter one (longest first), with the same heads per XCD
-            const int per = gridDim.x >> 3;
-            const int nh = per / numQB;
-            if (nh * numQB == per) {
-                const int xcd = w / per;
-                const int k = w - xcd * per;
-                qi = k / nh;
-                bh = xcd * nh + (k - qi * nh);
-            }
-        }
+        // causal: each XCD's range ordered by query block first (costliest blocks first)
+        work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL, bh, qi);
     }
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
