@@ -81,7 +81,8 @@ def test_bwd_on_the_oracle_forward_outputs(causal):
 
 
 @pytest.mark.parametrize("name,causal", [("b4h16n2k_d128", False), ("b4h16n2k_d128", True),
-                                         ("b4h16n8k_d128", False), ("b8h16n4k_d64", False)])
+                                         ("b4h16n8k_d128", False), ("b8h16n4k_d64", False),
+                                         ("b8h16n4k_d64", True), ("b4h16n8k_d128", True)])
 def test_bwd_full_size_sampled(name, causal):
     w = WORKLOADS[name]
     say(f"bwd workload {name} causal={causal} (sampled rows)")

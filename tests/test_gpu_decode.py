@@ -68,6 +68,17 @@ def test_decode_workloads_every_row(name):
     check(name, o, lse, o_ref, lse_ref)
 
 
+@pytest.mark.parametrize("Nq,causal", [(1, False), (3, True)])
+def test_decode_very_long_cache(Nq, causal):
+    # 262144 keys: 8192 tiles, the split count at its cap of 64
+    B, Hq, Hkv, Nk, d = 1, 8, 2, 262144, 128
+    say(f"decode long cache Nk={Nk} Nq={Nq} causal={causal}, workspace {fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)} B")
+    q, k, v = make_decode_inputs(B, Hq, Hkv, Nq, Nk, d, seed=33 + Nq)
+    o, lse = run(q, k, v, causal)
+    o_ref, lse_ref = attention_decode_fp64(q, k, v, d ** -0.5, causal)
+    check(f"Nk={Nk}", o, lse, o_ref, lse_ref)
+
+
 def test_decode_equals_forward_when_lengths_match():
     # Nq = Nk with one key/value head per query head is the forward problem
     B, H, N, d = 1, 3, 300, 128

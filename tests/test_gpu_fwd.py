@@ -139,6 +139,14 @@ def test_full_size_sampled(name, causal):
     check_sampled(WORKLOADS[name], causal)
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 65536, 128, False), (1, 2, 65536, 128, True),
+                                            (1, 1, 131072, 64, True)])
+def test_very_long_sequences_sampled(B, H, N, d, causal):
+    # row offsets and per-head byte counts far beyond the workloads (sampled rows)
+    from exact_attention_06_amd.workloads import Workload
+    check_sampled(Workload(f"long_b{B}h{H}n{N}_d{d}", B, H, N, d, "bf16", (causal,), 21), causal, n_heads=2, n_rows=96)
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 @pytest.mark.parametrize("d", [64, 128, 256])
