@@ -81,16 +81,32 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int | None:
+def _stream(stream, device) -> int | None:
+    """The HIP stream to launch on: the given one, else the current stream of the tensors'
+    device (not of whatever device happens to be current)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _require_gpu(*ts):
+    """Every tensor given is a contiguous GPU tensor and all of them sit on one device."""
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("attention tensors must be contiguous GPU tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"attention tensors must share one device ({dev} and {t.device})")
+
+
+def _expect(t, shape, dtype, name):
+    """A caller-provided output or workspace tensor has the shape and dtype the kernels write."""
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{name} must be {dtype} of shape {list(shape)}, got {t.dtype} {list(t.shape)}")
 
 
 def _bhnd(q):
@@ -122,10 +138,12 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, want_lse=True
         o = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _expect(o, (B, H, N, d), q.dtype, "o")
+    _expect(lse, (B, H, N), torch.float32, "lse")
     _require_gpu(q, k, v, o, lse)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale, int(bool(causal)), dt,
-                        _stream(stream)))
+                        _stream(stream, q.device)))
     return o, lse
 
 
@@ -144,8 +162,10 @@ def fa_prep_fp8(x, signs=None, x8=None, s=None, *, stream=None):
         s = torch.empty((B, H, nsb), dtype=torch.float32, device=x.device)
     if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d):
         raise ValueError("signs must be float32 with d entries")
+    _expect(x8, (B, H, N, d), torch.uint8, "x8")
+    _expect(s, (B, H, nsb), torch.float32, "s")
     _require_gpu(x, x8, s, signs)
-    _check(lib().fa_prep_fp8(_ptr(x), _ptr(x8), _ptr(s), _ptr(signs), B, H, N, d, _stream(stream)))
+    _check(lib().fa_prep_fp8(_ptr(x), _ptr(x8), _ptr(s), _ptr(signs), B, H, N, d, _stream(stream, x.device)))
     return x8, s
 
 
@@ -163,10 +183,12 @@ def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=F
         o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _expect(o, (B, H, N, d), torch.bfloat16, "o")
+    _expect(lse, (B, H, N), torch.float32, "lse")
     _require_gpu(q8, k8, v8, sq, sk, sv, o, lse)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk), _ptr(sv), _ptr(o), _ptr(lse),
-                            B, H, N, d, scale, int(bool(causal)), _stream(stream)))
+                            B, H, N, d, scale, int(bool(causal)), _stream(stream, q8.device)))
     return o, lse
 
 
@@ -188,10 +210,12 @@ def fa_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scal
     delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
     if delta.dtype != torch.float32 or delta.numel() < 2 * B * H * N:
         raise ValueError("delta must be a float32 workspace of 2*B*H*N elements")
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, (B, H, N, d), torch.bfloat16, name)
     _require_gpu(q, k, v, o, dout, lse, dq, dk, dv, delta)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(delta), B, H, N, d, scale, int(bool(causal)), FA_BF16, _stream(stream)))
+                        _ptr(delta), B, H, N, d, scale, int(bool(causal)), FA_BF16, _stream(stream, q.device)))
     return dq, dk, dv
 
 
@@ -214,6 +238,8 @@ def fa_decode(q, k, v, o=None, lse=None, workspace=None, *, scale=None, causal=F
     o = torch.empty_like(q) if o is None else o
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _expect(o, (B, Hq, Nq, d), torch.bfloat16, "o")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
     need = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -221,7 +247,7 @@ def fa_decode(q, k, v, o=None, lse=None, workspace=None, *, scale=None, causal=F
     _require_gpu(q, k, v, o, lse, workspace)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
-                           int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(stream)))
+                           int(bool(causal)), FA_BF16, _ptr(workspace), nbytes, _stream(stream, q.device)))
     return o, lse
 
 
@@ -253,9 +279,11 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, *, scale=None, causal=False, window=(-
     o = torch.empty_like(q) if o is None else o
     if lse is None and want_lse:
         lse = torch.empty((Bq, Hq, N), dtype=torch.float32, device=q.device)
+    _expect(o, (Bq, Hq, N, d), torch.bfloat16, "o")
+    _expect(lse, (Bq, Hq, N), torch.float32, "lse")
     _require_gpu(q, k, v, o, lse, cu_seqlens)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)
     _check(lib().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, scale,
                             int(bool(causal)), int(window[0]), int(window[1]), _ptr(cu_seqlens), int(max_seqlen),
-                            FA_BF16, _stream(stream)))
+                            FA_BF16, _stream(stream, q.device)))
     return o, lse

@@ -104,6 +104,50 @@ def test_python_binding_rejects_cpu_tensors(L):
         fa_fwd(q, q, q, o=torch.empty_like(q), lse=torch.empty(1, 1, 64))
 
 
+def test_python_binding_checks_given_outputs(L):
+    """Outputs the caller passes in are checked for shape and dtype before anything is
+    launched (an undersized one would be written past its end)."""
+    import torch
+
+    from exact_attention_06_amd import fa_bwd, fa_decode, fa_fwd, fa_fwd_ext, fa_fwd_fp8, fa_prep_fp8
+
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    lse = torch.empty(1, 2, 64)
+    with pytest.raises(ValueError, match="o must be"):
+        fa_fwd(q, q, q, o=torch.empty(1, 2, 32, 64, dtype=torch.bfloat16), lse=lse)
+    with pytest.raises(ValueError, match="o must be"):
+        fa_fwd(q, q, q, o=torch.empty(1, 2, 64, 64), lse=lse)            # float32 for bf16 inputs
+    with pytest.raises(ValueError, match="lse must be"):
+        fa_fwd(q, q, q, o=torch.empty_like(q), lse=torch.empty(2, 64))
+    with pytest.raises(ValueError, match="dk must be"):
+        fa_bwd(q, q, q, q, q, lse, dq=torch.empty_like(q), dk=torch.empty(1, 2, 64, 32, dtype=torch.bfloat16),
+               dv=torch.empty_like(q), delta=torch.empty(2, 1, 2, 64))
+    with pytest.raises(ValueError, match="lse must be"):
+        fa_decode(q[:, :, :4], q, q, o=torch.empty_like(q[:, :, :4]), lse=torch.empty(1, 2, 64))
+    with pytest.raises(ValueError, match="o must be"):
+        fa_fwd_ext(q, q[:, :1], q[:, :1], o=torch.empty(1, 1, 64, 64, dtype=torch.bfloat16))
+    x = torch.zeros(1, 2, 64, 64)
+    with pytest.raises(ValueError, match="s must be"):
+        fa_prep_fp8(x, x8=torch.empty(1, 2, 64, 64, dtype=torch.uint8), s=torch.empty(1, 2, 2))
+    c8 = torch.zeros(1, 2, 64, 64, dtype=torch.uint8)
+    sc = torch.ones(1, 2, 1)
+    with pytest.raises(ValueError, match="o must be"):
+        fa_fwd_fp8(c8, c8, c8, sc, sc, sc, o=torch.empty(1, 2, 64, 64))   # the fp8 forward writes bfloat16
+
+
+def test_python_binding_rejects_mixed_devices():
+    from types import SimpleNamespace
+
+    from exact_attention_06_amd._lib import _require_gpu
+
+    def fake(dev):
+        return SimpleNamespace(is_cuda=True, is_contiguous=lambda: True, device=dev)
+
+    _require_gpu(fake("cuda:0"), None, fake("cuda:0"))
+    with pytest.raises(ValueError, match="one device"):
+        _require_gpu(fake("cuda:0"), fake("cuda:1"))
+
+
 def bwd(L, ptrs=None, B=1, H=1, N=128, d=128, scale=0.088, causal=0, dtype=1):
     p = [P] * 10 if ptrs is None else ptrs
     return L.fa_bwd(*p, B, H, N, d, scale, causal, dtype, None)
