@@ -10,7 +10,11 @@
 //            flight, since vector-memory counters retire in order). (NQ 2 halves the LDS operand
 //            traffic per FLOP but needs one wave per SIMD with 512 registers; the compiler
 //            then spills and copies between register files, and it measured ~40% slower.)
-//   d = 256: BC 32, NQ 1, one workgroup per CU, not pipelined (registers)
+//   d = 256: BC 32, NQ 1, pipelined; 8 waves in pairs that split the head dimension (each
+//            wave holds Q and O for 128 columns: the d = 128 register footprint), one
+//            workgroup of 128 queries per CU. A wave holding all 256 columns needs more than
+//            the 256 VGPRs; the compiler then keeps O in AGPRs and copies all 128 accumulator
+//            registers every key block.
 #include "fa_fwd_kernel.h"
 #include "fa_internal.h"
 
@@ -26,19 +30,22 @@
 #ifndef FA_D128_PIPE
 #define FA_D128_PIPE 1
 #endif
+#ifndef FA_D256_SPLIT
+#define FA_D256_SPLIT 1
+#endif
 
 
 namespace fa {
 namespace {
 
-template <int D, int BC, int NQ, int MINB, bool PIPE, int WAVES = 4>
+template <int D, int BC, int NQ, int MINB, bool PIPE, int WAVES = 4, int DSPLIT = 1>
 hipError_t dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float scale,
                     bool causal, hipStream_t stream) {
     constexpr InKind K = InKind::BF16;
-    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE, WAVES>(q, k, v, nullptr, nullptr, nullptr, o, lse,
-                                                                         BH, N, scale, stream)
-                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE, WAVES>(q, k, v, nullptr, nullptr, nullptr, o, lse,
-                                                                          BH, N, scale, stream);
+    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE, WAVES, false, DSPLIT>(
+                        q, k, v, nullptr, nullptr, nullptr, o, lse, BH, N, scale, stream)
+                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE, WAVES, false, DSPLIT>(
+                        q, k, v, nullptr, nullptr, nullptr, o, lse, BH, N, scale, stream);
 }
 
 template <int D, int BC, int NQ, int MINB>
@@ -80,7 +87,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                                                                                     causal, stream);
             return dispatch<128, FA_D128_BC, FA_D128_NQ, FA_D128_MINB, FA_D128_PIPE != 0, 4>(q, k, v, o, lse, BH, N, scale,
                                                                                          causal, stream);
-        case 256: return dispatch<256, 32, 1, 1, false>(q, k, v, o, lse, BH, N, scale, causal, stream);
+        case 256:
+            if (FA_D256_SPLIT) return dispatch<256, 32, 1, 1, true, 8, 2>(q, k, v, o, lse, BH, N, scale, causal, stream);
+            return dispatch<256, 32, 1, 1, false>(q, k, v, o, lse, BH, N, scale, causal, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -125,7 +125,15 @@ struct FwdExt {
 // and V^T operand read from LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
 // PIPE: compute the scores of block j+1 while the softmax of block j runs (needs registers
 // for two score tiles); without it each block's scores are computed just before its softmax.
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES, bool EXT = false>
+// DSPLIT = 2: the head dimension is split over a pair of waves (waves 2w and 2w+1 own the same
+// 32 NQ queries). Each wave holds Q and the O accumulator for its half of d, computes its
+// half of the score contraction, and the two partial score tiles are exchanged through LDS at
+// the block barrier and added (fp32 addition commutes, so both waves see bit-identical scores
+// and take identical softmax decisions); each wave then accumulates its half of O. At
+// d = 256 this keeps a wave's registers at the d = 128 footprint, where a whole-d wave needs
+// more than the 256 VGPRs and the compiler copies the accumulator between register files.
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES, bool EXT = false,
+          int DSPLIT = 1>
 __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
@@ -136,19 +144,28 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     using C = FwdCfg<KIND, D, BC, NT>;
     using QT = typename QOperand<KIND>::type;
     constexpr float tau = (float)TAU;
-    constexpr int BR = WAVES * 32 * NQ;   // queries per workgroup
+    static_assert(DSPLIT == 1 || (DSPLIT == 2 && !C::F8 && PIPE && WAVES % 2 == 0), "d split: bf16, pipelined, wave pairs");
+    constexpr int BR = WAVES / DSPLIT * 32 * NQ;   // queries per workgroup
+    constexpr int KST = C::KSTEPS / DSPLIT;        // QK steps of one wave
+    constexpr int DTW = C::DT / DSPLIT;            // 32-wide d tiles of O^T of one wave
+    constexpr int XB = C::MT * NQ * 4096;          // bytes of one wave's partial score tiles
     // separate objects per buffer, so that the compiler can tell that LDS reads of one
     // buffer do not depend on the DMA writes still in flight into the other one
     __shared__ __attribute__((aligned(1024))) uint8_t smK0[C::K_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t smK1[C::K_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t smV0[C::V_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t smV1[C::V_BYTES];
+    // d split: partial score tiles of block parity 0 / 1, one XB region per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t smX0[DSPLIT > 1 ? WAVES * XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smX1[DSPLIT > 1 ? WAVES * XB : 16];
     uint8_t* const smK[2] = {smK0, smK1};
     uint8_t* const smV[2] = {smV0, smV1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
+    const int qwave = wave / DSPLIT;   // the wave's query tile(s)
+    const int hd = wave % DSPLIT;      // the wave's part of the head dimension
     const int h = lane >> 5;        // lane half
     const int col = lane & 31;      // query column owned by this lane in each query tile
 
@@ -166,7 +183,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     }
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
-    const int q0w = q0 + wave * 32 * NQ;
+    const int q0w = q0 + qwave * 32 * NQ;
     int qrow[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) qrow[n] = q0w + 32 * n + col;
@@ -234,13 +251,14 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 
     // ---- Q^T operands (B of S^T = K Q^T): in tile n the lane holds query qrow[n]; step s
     // covers head-dim elements [QK_K s + (QK_K/2) h, +QK_K/2)
-    QT qf[NQ][C::KSTEPS];
+    QT qf[NQ][KST];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         const bool ok = qrow[n] < N;
-        const uint8_t* qp = Qh + (size_t)(ok ? qrow[n] : 0) * C::ROW_BYTES + (C::QK_K / 2) * C::IN_BYTES * h;
+        const uint8_t* qp = Qh + (size_t)(ok ? qrow[n] : 0) * C::ROW_BYTES + (C::QK_K / 2) * C::IN_BYTES * h +
+                            hd * KST * C::QK_K * C::IN_BYTES;
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
+        for (int s = 0; s < KST; ++s) {
             const uint8_t* p = qp + s * C::QK_K * C::IN_BYTES;
             if constexpr (C::F8) {
                 const i32x4 lo = ok ? *(const i32x4*)p : i32x4{};
@@ -327,6 +345,9 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     constexpr int KREADS = C::F8 ? 2 : 1;              // 16-byte reads per operand
     constexpr int KSPAN = C::F8 ? 4 : 8;               // steps per 16 chunks
     constexpr int KA = C::KSTEPS < KSPAN ? C::KSTEPS : KSPAN;
+    static_assert(DSPLIT == 1 || (KST % KSPAN == 0 && DTW % 4 == 0), "d split: whole 16-chunk spans per wave");
+    const int khd = 256 * (hd * KST / KSPAN);   // the wave's first K chunk span
+    const int vhd = 256 * (hd * DTW / 4);       // and first V^T chunk span
     int kaddr[KA][KREADS];
     {
         const int rr = swap_bits23(col);   // same swizzle for rows rr and 32t + rr
@@ -356,13 +377,13 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     // rescale factor exp2(m_old - m_new) and the softmax bias need no special cases: a row
     // that has seen no key yet has l = 0, and masked scores are -inf whatever the bias.
     constexpr float kNoMax = -1e30f;
-    f32x16 acc[NQ][C::DT];
+    f32x16 acc[NQ][DTW];
     float m_run[NQ], l_run[NQ], m_blk[NQ];   // reference max, row sum, max of the next block
     bool grow[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
 #pragma unroll
-        for (int e = 0; e < C::DT; ++e) acc[n][e] = f32x16{};
+        for (int e = 0; e < DTW; ++e) acc[n][e] = f32x16{};
         m_run[n] = kNoMax;
         l_run[n] = 0.f;
         m_blk[n] = kNoMax;
@@ -379,10 +400,10 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 #pragma unroll
             for (int n = 0; n < NQ; ++n) st[t][n] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s)
+        for (int s = 0; s < KST; ++s)
 #pragma unroll
             for (int t = 0; t < C::MT; ++t) {
-                const uint8_t* p = kt + 32 * t * C::ROW_BYTES + 256 * (s / KSPAN);
+                const uint8_t* p = kt + 32 * t * C::ROW_BYTES + khd + 256 * (s / KSPAN);
                 if constexpr (C::F8) {
                     const i32x4 lo = *(const i32x4*)(p + kaddr[s % KSPAN][0]);
                     const i32x4 hi = *(const i32x4*)(p + kaddr[s % KSPAN][KREADS - 1]);
@@ -398,6 +419,34 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                         st[t][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n][s], st[t][n], 0, 0, 0);
                 }
             }
+    };
+    // d split: publish this wave's partial scores of a block (parity X), and add the partner
+    // wave's. Lane l stores its 16 values of a tile as four 16-byte chunks, chunk k of all
+    // lanes forming one contiguous 1 KB row (conflict-free); the partner's lane l holds the
+    // same (key, query) positions.
+    auto x_put = [&](f32x16 (*st)[NQ], auto x_c) {
+        uint8_t* xb = (decltype(x_c)::value ? smX1 : smX0) + wave * XB + 16 * lane;
+#pragma unroll
+        for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+            for (int n = 0; n < NQ; ++n)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    *(f32x4*)(xb + ((t * NQ + n) * 4 + k) * 1024) =
+                        f32x4{st[t][n][4 * k], st[t][n][4 * k + 1], st[t][n][4 * k + 2], st[t][n][4 * k + 3]};
+    };
+    auto x_add = [&](f32x16 (*st)[NQ], auto x_c) {
+        const uint8_t* xb = (decltype(x_c)::value ? smX1 : smX0) + (wave ^ 1) * XB + 16 * lane;
+#pragma unroll
+        for (int t = 0; t < C::MT; ++t)
+#pragma unroll
+            for (int n = 0; n < NQ; ++n)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const f32x4 o = *(const f32x4*)(xb + ((t * NQ + n) * 4 + k) * 1024);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) st[t][n][4 * k + u] += o[u];
+                }
     };
     // hide keys past N and, for the causal mask, keys after the query. Called only for
     // blocks that need it (the diagonal blocks and the ragged last block), unconditionally.
@@ -467,6 +516,12 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             if (needmask(j)) mask(s_cur, kb);
             row_max(s_cur, j);
         }
+        if constexpr (DSPLIT > 1) {
+            // the partner's half of block j's scores was published before the last barrier
+            x_add(s_cur, b_c);
+            if (needmask(j)) mask(s_cur, kb);
+            row_max(s_cur, j);
+        }
         // ---- move the reference max to block j's max where it grew past TAU, rescaling the row
         // sum and the accumulator by alpha = exp2(m_old - m_new) (rare with TAU > 0; elsewhere
         // alpha would be exactly 1, so the whole update is skipped)
@@ -481,7 +536,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 m_run[n] = m_ref;
                 l_run[n] *= alpha;
 #pragma unroll
-                for (int e = 0; e < C::DT; ++e)
+                for (int e = 0; e < DTW; ++e)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[n][e][i] *= alpha;
             }
@@ -519,13 +574,14 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         }
         // ---- scores of block j+1
         if constexpr (PIPE && NEXT) qk(smK[B ^ 1], s_nxt);
+        if constexpr (DSPLIT > 1 && NEXT) x_put(s_nxt, IC<B ^ 1>{});
         // ---- O^T += V_j^T P_j^T
         const uint8_t* vt = smV[B];
 #pragma unroll
         for (int ch = 0; ch < C::CH; ++ch)
 #pragma unroll
-            for (int e = 0; e < C::DT; ++e) {
-                const uint8_t* vp = vt + 16 * ch * C::VROW_BYTES + 256 * (e / 4) + vaddr[e % 4];
+            for (int e = 0; e < DTW; ++e) {
+                const uint8_t* vp = vt + 16 * ch * C::VROW_BYTES + vhd + 256 * (e / 4) + vaddr[e % 4];
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp));
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp + 4 * C::VROW_BYTES));
                 // concatenated as whole vectors (element-wise assembly is mis-compiled)
@@ -534,8 +590,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 for (int n = 0; n < NQ; ++n)
                     acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[n][ch], acc[n][e], 0, 0, 0);
             }
-        // ---- mask and row max of block j+1
-        if constexpr (PIPE && NEXT) {
+        // ---- mask and row max of block j+1 (d split: at the start of step j+1, after the exchange)
+        if constexpr (PIPE && NEXT && DSPLIT == 1) {
             if constexpr (MASKN) mask(s_nxt, kb + BC);
             row_max(s_nxt, j + 1);
         }
@@ -557,9 +613,16 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     __syncthreads();
     if constexpr (PIPE) {
         qk(smK[0], s_buf[0]);
-        if (needmask(jlo)) mask(s_buf[0], kb0);
-        row_max(s_buf[0], jlo);
-        __syncthreads();   // every wave is done with smK[0] before block 0 refills it
+        if constexpr (DSPLIT > 1) {
+            x_put(s_buf[0], IC<0>{});
+        } else {
+            if (needmask(jlo)) mask(s_buf[0], kb0);
+            row_max(s_buf[0], jlo);
+        }
+        // every wave is done with smK[0] before block 0 refills it (and has published its
+        // partial scores of block 0)
+        if constexpr (DSPLIT > 1) __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     // blocks in pairs (block jlo + even in buffer 0); block j+1's mask is needed iff
@@ -593,7 +656,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     // tile of O in LDS (the tile slots are free after the last barrier) and writes it back in
     // whole rows, 16 bytes per lane: a lane's own results are 4-element runs scattered over
     // the d range, which would make every store instruction touch 32 rows.
-    constexpr int OROW = D * 2;                        // bytes per bf16 row of O
+    constexpr int DW = D / DSPLIT;                     // columns of O this wave writes
+    constexpr int OROW = DW * 2;                       // bytes per staged bf16 row
     constexpr int OSTAGE = 32 * OROW;                  // one wave's tile
     constexpr int OSW = (OROW / 16 < 16 ? OROW / 16 : 16) - 1;   // XOR mask of the 16-byte chunks
     constexpr bool KFITS = C::K_BYTES >= OSTAGE;       // V slots always fit (BC >= 32 rows)
@@ -616,7 +680,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 // result register 4a + b of d tile e holds d = 32 e + 8 a + 4 h + b of query col:
                 // 16-byte chunk 4 e + a of the row, half h
 #pragma unroll
-                for (int e = 0; e < C::DT; ++e)
+                for (int e = 0; e < DTW; ++e)
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         bf16x4 ov;
@@ -624,7 +688,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                         for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[n][e][4 * a + b] * inv);
                         *(bf16x4*)(stg + col * OROW + 16 * ((4 * e + a) ^ (col & OSW)) + 8 * h) = ov;
                     }
-                if (LSE != nullptr && h == 0 && qrow[n] < N)
+                if (LSE != nullptr && h == 0 && hd == 0 && qrow[n] < N)
                     LSE[qbase + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
                 // the wave reads back what its other lanes wrote
                 __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -635,7 +699,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                     const int r = RPI * it + lane / LPR;
                     const int c = lane % LPR;
                     const i32x4 v = *(const i32x4*)(stg + r * OROW + 16 * (c ^ (r & OSW)));
-                    if (qt0 + r < N) *(i32x4*)((uint8_t*)(O + head_off + (size_t)(qt0 + r) * D) + 16 * c) = v;
+                    if (qt0 + r < N) *(i32x4*)((uint8_t*)(O + head_off + (size_t)(qt0 + r) * D + hd * DW) + 16 * c) = v;
                 }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
                 __builtin_amdgcn_wave_barrier();
@@ -647,16 +711,17 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 
 // EXT kernels: BH = (sequences or batches) x Hq workgroup rows, N = the longest sequence (the
 // grid's query blocks), ext as described at FwdExt
-template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES = 4, bool EXT = false>
+template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bool PIPE, int WAVES = 4, bool EXT = false,
+          int DSPLIT = 1>
 hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const float* sq, const float* sk,
                              const float* sv, void* o, float* lse, int BH, int N, float scale, hipStream_t stream,
                              FwdExt ext = FwdExt{}) {
-    constexpr int BR = WAVES * 32 * NQ;
+    constexpr int BR = WAVES / DSPLIT * 32 * NQ;
     const int numQB = (N + BR - 1) / BR;
     const int nsb = (N + 63) / 64;
     const long long total = (long long)BH * numQB;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT>), dim3((unsigned)total),
+    hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT, DSPLIT>), dim3((unsigned)total),
                        dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e, ext);
     return hipGetLastError();
 }
