@@ -177,6 +177,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
             ta.load(rK, (B ? sK0 : sK1), kb + BC, wave);
             ta.load(rV, (B ? sV0 : sV1), kb + BC, wave);
         }
+        // issue the loads here: left to itself the scheduler sinks them to the end of the step,
+        // just before the wait for them
+        __builtin_amdgcn_sched_barrier(0);
         // S^T = K Q^T and dP^T = V dO^T (keys x queries)
         // dP^T - D: the product starts from -D (the query's, in every register)
         f32x16 st{}, dpt;
@@ -281,27 +284,45 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
         dv[e] = f32x16{};
     }
 
-    auto step = [&](int i, auto b_c, auto mask_c) __attribute__((always_inline)) {
-        constexpr int B = decltype(b_c)::value;
-        constexpr bool MASK = decltype(mask_c)::value != 0;
-        const int q0 = i * BQ;
-        if (i + 1 < nqb) {
-            ta.load(rQ, (B ? sQ0 : sQ1), q0 + BQ, wave);
-            ta.load(rO, (B ? sD0 : sD1), q0 + BQ, wave);
-        }
-        // -LSE log2(e) and D of the queries this lane half holds: tile tt, rows
-        // q0 + 32 tt + 16u + 8h + 0..7
-        f32x4 lq[QT][4], dq[QT][4];
+    // -LSE log2(e) and -D of the queries this lane half holds in query block i: tile tt, rows
+    // i BQ + 32 tt + 16u + 8h + 0..7. Loaded one step ahead (rows past N read as zero): the
+    // loads for block i + 1 are issued at the start of step i, ahead of its tile loads, and
+    // complete by its end, so no step waits for them
+    f32x4 lq_n[QT][4], dq_n[QT][4];
+    auto load_rows = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int tt = 0; tt < QT; ++tt)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int v2 = 0; v2 < 2; ++v2) {
-                    const int off = 4 * (q0 + 32 * tt + 16 * u + 8 * h + 4 * v2);
-                    lq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
-                    if constexpr (DOK) dq[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+                    const int off = 4 * (i * BQ + 32 * tt + 16 * u + 8 * h + 4 * v2);
+                    lq_n[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
+                    if constexpr (DOK) dq_n[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
                 }
+    };
+
+    auto step = [&](int i, auto b_c, auto mask_c) __attribute__((always_inline)) {
+        constexpr int B = decltype(b_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value != 0;
+        const int q0 = i * BQ;
+        f32x4 lq[QT][4], dq[QT][4];
+#pragma unroll
+        for (int tt = 0; tt < QT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                lq[tt][r] = lq_n[tt][r];
+                if constexpr (DOK) dq[tt][r] = dq_n[tt][r];
+            }
+        load_rows(i + 1);
+        // the next tiles, issued here (left to itself the scheduler sinks the loads to the end
+        // of the step, just before the wait for them)
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < nqb) {
+            ta.load(rQ, (B ? sQ0 : sQ1), q0 + BQ, wave);
+            ta.load(rO, (B ? sD0 : sD1), q0 + BQ, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // S = Q K^T and dP = dO V^T (queries x keys), per 32-query tile
         f32x16 s[QT], dp[QT];
 #pragma unroll
@@ -351,6 +372,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
     };
 
     if (i0 < nqb) {
+        load_rows(i0);
         ta.load(rQ, sQ0, i0 * BQ, wave);
         ta.load(rO, sD0, i0 * BQ, wave);
         __builtin_amdgcn_s_waitcnt(0);
@@ -413,10 +435,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     constexpr int TB = C::TB;          // one 32-row tile
     static_assert(C::LOADS == 1, "one load region per wave and tile");
     constexpr int PT = 64 * 16 * 4;    // one P tile: 16 fp32 per lane, stored as 4 planes of 16 B per lane
-    constexpr int OQ = 0, OD = 3 * TB, OP = 6 * TB;
-    constexpr int LDS_BYTES = OP + 12 * PT;
-    static_assert(LDS_BYTES >= W * TB, "the output staging reuses the tile slots");
-    __shared__ __attribute__((aligned(1024))) uint8_t sm[LDS_BYTES];
+    // one LDS object per tile slot (three each for Q and dO), so that the compiler can tell
+    // that reads of one slot do not touch the DMA writes still in flight into another (with
+    // one array it waits for every tile load before each transposing read); and the P tiles
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ1[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sQ2[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sD0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sD1[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sD2[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sP[12 * PT];
+    static_assert(6 * TB + 12 * PT >= W * TB && 12 * PT >= (W - 6) * TB, "the output staging reuses the slots");
+    auto qslot = [&](int t) __attribute__((always_inline)) { return t == 0 ? sQ0 : t == 1 ? sQ1 : sQ2; };
+    auto dslot = [&](int t) __attribute__((always_inline)) { return t == 0 ? sD0 : t == 1 ? sD1 : sD2; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -452,11 +483,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
     const int hi = max(lo, N / BQ);
     const int u = max(lo, i0 + 1);   // first block of the unrolled loops (the first block is peeled)
-    uint8_t* const pbuf = sm + OP + 3 * PT * pair;
+    uint8_t* const pbuf = sP + 3 * PT * pair;
     auto slot = [&](int i) __attribute__((always_inline)) { return ((i - u) % 3 + 3) % 3; };
     auto load_tiles = [&](int i, int t) __attribute__((always_inline)) {
-        if (LW == W || pwave) ta.load(rQ, sm + OQ + TB * t, i * BQ, lwave);
-        if (LW == W || !pwave) ta.load(rO, sm + OD + TB * t, i * BQ, lwave);
+        if (LW == W || pwave) ta.load(rQ, qslot(t), i * BQ, lwave);
+        if (LW == W || !pwave) ta.load(rO, dslot(t), i * BQ, lwave);
     };
     // four values per lane from a per-query fp32 vector: registers 4v .. 4v+3 of tile rows
     // q0 + 16(v/2) + 8h + 4(v%2) + 0..3
@@ -465,6 +496,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         for (int v = 0; v < 4; ++v)
             x[v] = __builtin_bit_cast(f32x4, buffer_load16(r, 4 * (q0 + 16 * (v / 2) + 8 * h + 4 * (v % 2))));
     };
+
+    // the row values of the wave's next step, loaded one step ahead (see the dK/dV kernel):
+    // -LSE log2(e) (P wave) or -D (dS wave)
+    f32x4 rv_n[4];
 
     bf16x8 pf[2];   // P wave: P of the previous block, the B operand of its dV product
     auto dv_update = [&](const uint8_t* td) __attribute__((always_inline)) {
@@ -481,12 +516,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         constexpr bool MASK = decltype(mask_c)::value != 0;
         constexpr bool FIRST = decltype(first_c)::value != 0;
         const int t = SL >= 0 ? SL : slot(i);
-        if (i + 1 < nqb) load_tiles(i + 1, SL >= 0 ? (SL + 1) % 3 : slot(i + 1));
-        if constexpr (!FIRST) dv_update(sm + OD + TB * (SL >= 0 ? (SL + 2) % 3 : slot(i - 1)));
         const int q0 = i * BQ;
-        const uint8_t* tq = sm + OQ + TB * t;
+        // the next step's row values ahead of the tile loads: vector-memory counters retire in
+        // order, so a wait for values loaded after the tiles would also wait for the tiles
         f32x4 lq[4];   // -LSE log2(e)
-        row_vals(rL, q0, lq);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lq[v] = rv_n[v];
+        row_vals(rL, q0 + BQ, rv_n);
+        __builtin_amdgcn_sched_barrier(0);
+        // (the unrolled steps, SL >= 0, always have a next block: no branch around the loads)
+        if (SL >= 0 || i + 1 < nqb) load_tiles(i + 1, SL >= 0 ? (SL + 1) % 3 : slot(i + 1));
+        __builtin_amdgcn_sched_barrier(0);   // and issued early, not sunk to the end of the step
+        if constexpr (!FIRST) dv_update(dslot(SL >= 0 ? (SL + 2) % 3 : slot(i - 1)));
+        const uint8_t* tq = qslot(t);
         f32x16 sc{};
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
@@ -512,15 +554,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     auto step_ds = [&](int i, auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value;
         const int t = SL >= 0 ? SL : slot(i);
-        if (i + 2 < nqb) load_tiles(i + 2, SL >= 0 ? (SL + 2) % 3 : slot(i + 2));
         const int q0 = i * BQ;
-        const uint8_t* tq = sm + OQ + TB * t;
-        const uint8_t* td = sm + OD + TB * t;
-        f32x4 dl[4];   // -D, in the register layout of dP
-        row_vals(rDl, q0, dl);
-        // dP, then dP - D (the -D loads are in flight while the product runs; starting the
-        // product from -D would make it wait for them)
-        f32x16 dp{};
+        f32x4 dl[4];   // -D, in the register layout of dP (the next step's loaded as above)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dl[v] = rv_n[v];
+        row_vals(rDl, q0 + BQ, rv_n);
+        __builtin_amdgcn_sched_barrier(0);
+        if (SL >= 0 || i + 2 < nqb) load_tiles(i + 2, SL >= 0 ? (SL + 2) % 3 : slot(i + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* tq = qslot(t);
+        const uint8_t* td = dslot(t);
+        // dP - D: the product starts from -D (loaded a step ago)
+        f32x16 dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = dl[r / 4][r % 4];
 #pragma unroll
         for (int st = 0; st < C::KSTEPS; ++st)
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand(td, st), kv[st], dp, 0, 0, 0);
@@ -530,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         for (int j = 0; j < 4; ++j) pv[j] = *(const f32x4*)(pb + 1024 * j);
         bf16x8 dsf[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsf[r / 8][r % 8] = (bf16_t)(pv[r / 4][r % 4] * (dp[r] + dl[r / 4][r % 4]));
+        for (int r = 0; r < 16; ++r) dsf[r / 8][r % 8] = (bf16_t)(pv[r / 4][r % 4] * dp[r]);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
@@ -544,6 +591,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         // both kinds of wave take part in every tile load and in every barrier: nqb - i0 + 1
         // steps after the first load, the P waves' blocks in steps 0 .. nqb - i0 - 1, the dS
         // waves' in steps 1 .. nqb - i0
+        row_vals(pwave ? rL : rDl, i0 * BQ, rv_n);
         load_tiles(i0, slot(i0));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -560,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
             }
             // the rest (masking blocks below hi is harmless), then dV of the last block
             for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
-            dv_update(sm + OD + TB * slot(nqb - 1));
+            dv_update(dslot(slot(nqb - 1)));
             __syncthreads();
         } else {
             if (i0 + 1 < nqb) load_tiles(i0 + 1, slot(i0 + 1));
@@ -577,7 +625,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     }
 
     // dV = dV~, dK = scale dK~; each wave stages its 32-key tile in its own 32-row slot
-    store_rows<D>(acc, pwave ? 1.f : scale, sm + TB * wave, (pwave ? dV : dK) + head, k0w, N, lane);
+    uint8_t* const stg = wave < 3 ? qslot(wave) : wave < 6 ? dslot(wave - 3) : sP + (wave - 6) * TB;
+    store_rows<D>(acc, pwave ? 1.f : scale, stg, (pwave ? dV : dK) + head, k0w, N, lane);
 }
 
 // dK and dV: one pass at d = 64; at d = 128 the two accumulators need more registers than two
