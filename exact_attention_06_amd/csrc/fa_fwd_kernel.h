@@ -472,6 +472,16 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     int nfull;
     if (right >= 0) nfull = min(N / BC, (q0 + right + 1) / BC);
     else nfull = N / BC;
+    // causal (not windowed): each wave computes only the key blocks its own queries reach
+    // (nkb_c) and masks only the ones that straddle its own diagonal (from nfull on); it still
+    // loads its share of the workgroup's later blocks, which the other waves need, and takes
+    // part in their barriers
+    constexpr bool PER_WAVE = CAUSAL && !EXT;
+    int nkb_c = nkb;
+    if constexpr (PER_WAVE) {
+        nkb_c = min(nkb, (min(q0w + 32 * NQ, N) - 1) / BC + 1);
+        nfull = min(N / BC, (q0w + 1) / BC);
+    }
     auto needmask = [&](int x) { return x >= nfull || (EXT && x < jfree); };
     auto kscale = [&](int jj) {
         if constexpr (C::F8) return SK[(size_t)bh * nsb + jj * BC / 64];
@@ -508,9 +518,10 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         if constexpr (PIPE) {
             if (j + 2 < nkb) load_k(kb + 2 * BC, smK[B]);
         } else {
-            if (NEXT) load_k(kb + BC, smK[B ^ 1]);
+            if (NEXT || (PER_WAVE && j + 1 < nkb)) load_k(kb + BC, smK[B ^ 1]);
         }
-        if (NEXT) load_v(kb + BC, smV[B ^ 1]);
+        // (per-wave causal: the workgroup may need block j+1 when this wave is done)
+        if (NEXT || (PER_WAVE && j + 1 < nkb)) load_v(kb + BC, smV[B ^ 1]);
         if constexpr (!PIPE) {
             qk(smK[B], s_cur);
             if (needmask(j)) mask(s_cur, kb);
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             row_max(s_nxt, j + 1);
         }
         if constexpr (C::F8) {
-            if (NEXT) store_v(smV[B ^ 1]);
+            if (NEXT || (PER_WAVE && j + 1 < nkb)) store_v(smV[B ^ 1]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -635,21 +646,42 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
         }
     }
-    for (; j + 2 < nkb && j + 2 < nfull; j += 2) {
+    for (; j + 2 < nkb_c && j + 2 < nfull; j += 2) {
         step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<1>{}, IC<0>{});
     }
-    for (; j + 2 < nkb; j += 2) {
+    for (; j + 2 < nkb_c; j += 2) {
         if (needmask(j + 1)) step(j, IC<0>{}, IC<1>{}, IC<1>{});
         else step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
     }
-    if (j + 1 < nkb) {
+    if (j + 1 < nkb_c) {
         if (needmask(j + 1)) step(j, IC<0>{}, IC<1>{}, IC<1>{});
         else step(j, IC<0>{}, IC<1>{}, IC<0>{});
         step(j + 1, IC<1>{}, IC<0>{}, IC<0>{});
     } else {
         step(j, IC<0>{}, IC<0>{}, IC<0>{});
+    }
+    if constexpr (PER_WAVE) {
+        // the workgroup's blocks past this wave's queries: its share of their loads, and
+        // their barriers (every wave passes nkb - jlo barriers in the loop)
+        for (int jj = nkb_c; jj < nkb; ++jj) {
+            const int kb = jj * BC;
+            const bool odd = ((jj - jlo) & 1) != 0;   // buffer parity of block jj (selects, not a
+                                                      // run-time index into the pointer pairs)
+            if constexpr (PIPE) {
+                if (jj + 2 < nkb) load_k(kb + 2 * BC, odd ? smK1 : smK0);
+            } else {
+                if (jj + 1 < nkb) load_k(kb + BC, odd ? smK0 : smK1);
+            }
+            if (jj + 1 < nkb) {
+                uint8_t* const vn = odd ? smV0 : smV1;
+                load_v(kb + BC, vn);
+                store_v(vn);   // FP8: the staged V, expanded (the loads are awaited first)
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2. Each wave stages its 32 x d bf16
