@@ -472,15 +472,17 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     int nfull;
     if (right >= 0) nfull = min(N / BC, (q0 + right + 1) / BC);
     else nfull = N / BC;
-    // causal (not windowed): each wave computes only the key blocks its own queries reach
-    // (nkb_c) and masks only the ones that straddle its own diagonal (from nfull on); it still
-    // loads its share of the workgroup's later blocks, which the other waves need, and takes
-    // part in their barriers
-    constexpr bool PER_WAVE = CAUSAL && !EXT;
+    // causal or a window's right edge: each wave computes only the key blocks its own queries
+    // reach (nkb_c) and masks only the ones that cross its own right edge (from nfull on); it
+    // still loads its share of the workgroup's later blocks, which the other waves need, and
+    // takes part in their barriers
+    constexpr bool PER_WAVE = CAUSAL || EXT;
     int nkb_c = nkb;
     if constexpr (PER_WAVE) {
-        nkb_c = min(nkb, (min(q0w + 32 * NQ, N) - 1) / BC + 1);
-        nfull = min(N / BC, (q0w + 1) / BC);
+        if (right >= 0) {
+            nkb_c = min(nkb, (min(q0w + 32 * NQ, N) - 1 + right) / BC + 1);
+            nfull = min(N / BC, (q0w + right + 1) / BC);
+        }
     }
     auto needmask = [&](int x) { return x >= nfull || (EXT && x < jfree); };
     auto kscale = [&](int jj) {
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     int j = jlo;
     if constexpr (EXT) {
         // the window's lower edge: the next block reaches below some query's window
-        for (; j + 2 < nkb && j + 1 < jfree; j += 2) {
+        for (; j + 2 < nkb_c && j + 1 < jfree; j += 2) {
             step(j, IC<0>{}, IC<1>{}, IC<1>{});
             step(j + 1, IC<1>{}, IC<1>{}, IC<1>{});
         }
