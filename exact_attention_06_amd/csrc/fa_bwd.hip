@@ -161,8 +161,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
 
     int nkb = (N + BC - 1) / BC;
     if (CAUSAL) nkb = min(nkb, (min(q0 + BR, N) - 1) / BC + 1);
-    // blocks [0, nfull) need no mask for any query of the workgroup
-    const int nfull = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
+    // causal: the wave computes only the key blocks its own 32 queries reach (nkb_c) and masks
+    // only those that straddle its own diagonal (from nfull on); it loads its share of the
+    // workgroup's later blocks, which the other waves need, and takes part in their barriers.
+    // Blocks [0, nfull) need no mask for any query of the wave.
+    const int nkb_c = CAUSAL ? min(nkb, (min(q0w + 32, N) - 1) / BC + 1) : nkb;
+    const int nfull = CAUSAL ? min(N / BC, (q0w + 1) / BC) : N / BC;
 
     f32x16 acc[C::DT];
 #pragma unroll
@@ -214,14 +218,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int j = 0;
-    for (; j + 1 < nkb && j + 1 < nfull; j += 2) {
+    for (; j + 1 < nkb_c && j + 1 < nfull; j += 2) {
         step(j, BIC<0>{}, BIC<0>{});
         step(j + 1, BIC<1>{}, BIC<0>{});
     }
-    for (; j < nkb; j += 2) {
+    for (; j < nkb_c; j += 2) {
         if (j >= nfull) step(j, BIC<0>{}, BIC<1>{});
         else step(j, BIC<0>{}, BIC<0>{});
-        if (j + 1 < nkb) step(j + 1, BIC<1>{}, BIC<1>{});
+        if (j + 1 < nkb_c) step(j + 1, BIC<1>{}, BIC<1>{});
+    }
+    if constexpr (CAUSAL) {
+        // blocks past this wave's queries: loads and barriers only (every wave passes nkb)
+        for (int jj = nkb_c; jj < nkb; ++jj) {
+            if (jj + 1 < nkb) {
+                const bool odd = (jj & 1) != 0;   // block jj + 1 goes to buffer (jj + 1) & 1
+                ta.load(rK, odd ? sK0 : sK1, (jj + 1) * BC, wave);
+                ta.load(rV, odd ? sV0 : sV1, (jj + 1) * BC, wave);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     }
 
     // dQ = scale dQ~ (each wave stages its tile in one of the four tile buffers; with 8 waves
@@ -385,6 +401,19 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
         const int nfree_hi = N / BQ;                                              // full blocks end here
         const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;   // blocks from here see all keys
         const int hi = max(lo, nfree_hi);
+        // causal: query blocks before iw see none of this wave's keys; for the wave they are
+        // loads and barriers only (the other waves need the tiles)
+        const int iw = CAUSAL ? min(lo, max(i0, k0w / BQ)) : i0;
+        for (int i = i0; i < iw; ++i) {
+            load_rows(i + 1);
+            if (i + 1 < nqb) {
+                const bool odd = ((i - i0) & 1) != 0;   // block i + 1 goes to slot (i + 1 - i0) & 1
+                ta.load(rQ, odd ? sQ0 : sQ1, (i + 1) * BQ, wave);
+                ta.load(rO, odd ? sD0 : sD1, (i + 1) * BQ, wave);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
         auto run = [&](int a, int b, auto mask_c) __attribute__((always_inline)) {   // blocks [a, b), all masked or all not
             if (a >= b) return;
             if ((a - i0) & 1) step(a++, BIC<1>{}, mask_c);
@@ -394,7 +423,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
             }
             if (a < b) step(a, BIC<0>{}, mask_c);
         };
-        run(i0, lo, BIC<1>{});
+        run(iw, lo, BIC<1>{});
         run(lo, hi, BIC<0>{});
         run(hi, nqb, BIC<1>{});
     }
@@ -483,6 +512,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const int lo = CAUSAL ? min(nqb, (k0 + BK + BQ - 1) / BQ) : i0;
     const int hi = max(lo, N / BQ);
     const int u = max(lo, i0 + 1);   // first block of the unrolled loops (the first block is peeled)
+    // causal: query blocks before ip see none of this pair's keys; for the pair they are
+    // loads and barriers only (the other pairs need the tiles)
+    const int ip = CAUSAL ? min(nqb, max(i0, k0w / BQ)) : i0;
     uint8_t* const pbuf = sP + 3 * PT * pair;
     auto slot = [&](int i) __attribute__((always_inline)) { return ((i - u) % 3 + 3) % 3; };
     auto load_tiles = [&](int i, int t) __attribute__((always_inline)) {
@@ -599,21 +631,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
         // compiler copy the accumulators on every iteration)
         int i = i0;
         if (pwave) {
-            step_p(i++, BIC<-1>{}, BIC<1>{}, BIC<1>{});
-            for (; i < u; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
-            for (; i + 3 <= hi; i += 3) {
-                step_p(i, BIC<0>{}, BIC<0>{}, BIC<0>{});
-                step_p(i + 1, BIC<1>{}, BIC<0>{}, BIC<0>{});
-                step_p(i + 2, BIC<2>{}, BIC<0>{}, BIC<0>{});
+            for (; i < ip; ++i) {   // blocks before the pair's keys
+                row_vals(rL, (i + 1) * BQ, rv_n);
+                if (i + 1 < nqb) load_tiles(i + 1, slot(i + 1));
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
             }
-            // the rest (masking blocks below hi is harmless), then dV of the last block
-            for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
-            dv_update(dslot(slot(nqb - 1)));
+            if (i < nqb) {
+                step_p(i++, BIC<-1>{}, BIC<1>{}, BIC<1>{});
+                for (; i < u; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
+                for (; i + 3 <= hi; i += 3) {
+                    step_p(i, BIC<0>{}, BIC<0>{}, BIC<0>{});
+                    step_p(i + 1, BIC<1>{}, BIC<0>{}, BIC<0>{});
+                    step_p(i + 2, BIC<2>{}, BIC<0>{}, BIC<0>{});
+                }
+                // the rest (masking blocks below hi is harmless), then dV of the last block
+                for (; i < nqb; ++i) step_p(i, BIC<-1>{}, BIC<1>{}, BIC<0>{});
+                dv_update(dslot(slot(nqb - 1)));
+            }
             __syncthreads();
         } else {
             if (i0 + 1 < nqb) load_tiles(i0 + 1, slot(i0 + 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            for (; i < ip; ++i) {   // blocks before the pair's keys, one step behind the P wave
+                row_vals(rDl, (i + 1) * BQ, rv_n);
+                if (i + 2 < nqb) load_tiles(i + 2, slot(i + 2));
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
             for (; i < u; ++i) step_ds(i, BIC<-1>{});
             for (; i + 3 <= nqb; i += 3) {
                 step_ds(i, BIC<0>{});
