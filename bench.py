@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -73,14 +74,23 @@ def parse_args():
 HEADLINE_SOURCES = ("fa_common.h", "fa_fwd_kernel.h", "fa_fwd_bf16.hip")
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, whitespace collapsed (the kernel sources hold no string
+    literals with comment markers): what the compiler sees, so that editing a comment does not
+    make stored measurements of the code stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the headline kernel's sources, to tell whether stored counter readings of that
-    kernel are still current."""
+    """Hash of the headline kernel's sources (code only), to tell whether stored counter
+    readings of that kernel are still current."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
     for name in HEADLINE_SOURCES:
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(code_only(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()[:16]
 
 

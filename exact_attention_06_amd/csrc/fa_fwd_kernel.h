@@ -1,14 +1,15 @@
 // The fused attention forward kernel shared by the bf16 and the e4m3 (FP8) inputs.
 //
 // Algorithm: the FA2 loop order ("FlashAttention 2 & 3: Work Partitioning, Warp
-// Specialization & FP8", sections "Edit 1" to "Edit 3"): one workgroup owns 128 queries of
-// one (batch, head) and streams every key/value block of that head through LDS, keeping the
+// Specialization & FP8", sections "Edit 1" to "Edit 3"): one workgroup owns 128 (or 256)
+// queries of one (batch, head) and streams every key/value block of that head through LDS, keeping the
 // online-softmax state ("Learn: The Memory Wall & FlashAttention", section 5.1: running max
 // m, running sum l, unnormalised accumulator o) in registers; the division by l happens once
 // at the end, together with the logsumexp L = m + log l.
 //
 // CDNA4 mapping:
-// - 4 waves x 32 queries. Each wave computes S^T = K_j Q_i^T (keys x queries) on the matrix
+// - 4 or 8 waves x 32 queries (at d = 256, 8 waves in pairs that split the head dimension).
+//   Each wave computes S^T = K_j Q_i^T (keys x queries) on the matrix
 //   cores (bf16: v_mfma_f32_32x32x16_bf16; FP8: v_mfma_scale_f32_32x32x64_f8f6f4 with unit
 //   MX scales), so the scores of one query sit in one lane (16 per 32-key tile) and its
 //   partner lane l^32: row max and row sum are in-register reductions plus one
@@ -28,10 +29,11 @@
 // - The accumulator is rescaled only when a row maximum grows by more than 2^TAU (the
 //   conditional rescaling of the FA4 section of the memory-wall page). The result stays
 //   exact (numerator and denominator use the same reference); P is bounded by 2^TAU.
-// - Causal: key blocks entirely above the workgroup's diagonal are never visited; only
-//   blocks that straddle the diagonal are masked element by element. Each head's query
-//   blocks are walked heaviest first, and the XCD-aware remap keeps a head's blocks on one
-//   XCD (one L2).
+// - Causal: key blocks entirely above the workgroup's diagonal are never visited; a wave
+//   computes only the blocks its own queries reach and masks element by element only the
+//   blocks that straddle its own diagonal (it still helps load the workgroup's later blocks).
+//   Each head's query blocks are walked heaviest first, and the XCD-aware remap keeps a
+//   head's blocks on one XCD (one L2).
 //
 // FP8 inputs ("FlashAttention-3: How Warp Specialization ...", section 4 "Technique 3";
 // "FlashAttention 2 & 3", section "What stays in higher precision"):
