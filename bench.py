@@ -221,8 +221,8 @@ def cpu_baseline(w, budget_s: float = 15.0):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention forward "
-              "is not sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs "
+              "on one GPU per call and the attention forward is not sharded across GPUs.", file=sys.stderr)
         return 2
     import torch
 
