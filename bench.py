@@ -407,7 +407,18 @@ def main():
                            "TFLOP/s_warm": round(wx.flops(False) / warm["median"] / 1e9, 2)}
             progress(f"{name}: warm {warm['median']:.4f} ms, cold {cold['median']:.4f} ms")
             del q, k, v, o, lse
-        del scratch
+        # what the same protocol allows: a device copy moving the bytes of the N = 128 shape
+        # (half read, half written), warm and after the same flush
+        nb = extra["short_b64h16n128_d128"]["bytes"]
+        src = torch.empty(nb // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        cp = lambda: dst.copy_(src)
+        ramp(torch, cp, 30.0)
+        cw, cc = launch_stats(torch, cp, 20), launch_stats(torch, cp, 20, flush)
+        extra["copy_same_bytes_as_n128"] = {"bytes": 2 * (nb // 2), "warm_GB/s": round(2 * (nb // 2) / cw["median"] / 1e6, 1),
+                                            "cold_GB/s": round(2 * (nb // 2) / cc["median"] / 1e6, 1)}
+        del scratch, src, dst
         from exact_attention_06_amd.workloads import DECODE_WORKLOADS
         for name in ("decode_b16_hq32_hkv8_nk8k_d128", "decode_b2_h32_nk32k_d128"):
             extra[name] = decode_case(DECODE_WORKLOADS[name], args.steps, args.warmup, 100.0)

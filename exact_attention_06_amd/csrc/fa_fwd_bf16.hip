@@ -10,6 +10,7 @@
 //            flight, since vector-memory counters retire in order). (NQ 2 halves the LDS operand
 //            traffic per FLOP but needs one wave per SIMD with 512 registers; the compiler
 //            then spills and copies between register files, and it measured ~40% slower.)
+//   N <= 128 (d = 64, 128): the short-sequence kernel (fa_fwd_short.hip)
 //   d = 256: BC 32, NQ 1, pipelined; 8 waves in pairs that split the head dimension (each
 //            wave holds Q and O for 128 columns: the d = 128 register footprint), one
 //            workgroup of 128 queries per CU. A wave holding all 256 columns needs more than
@@ -29,6 +30,9 @@
 #endif
 #ifndef FA_D128_PIPE
 #define FA_D128_PIPE 1
+#endif
+#ifndef FA_SHORT
+#define FA_SHORT 1
 #endif
 #ifndef FA_D256_SPLIT
 #define FA_D256_SPLIT 1
@@ -76,6 +80,8 @@ hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream) {
+    // a whole head in one workgroup's LDS (fa_fwd_short.hip)
+    if (FA_SHORT && short_fwd_applies(N, d)) return launch_fwd_short_bf16(q, k, v, o, lse, BH, N, d, scale, causal, stream);
     switch (d) {
         case 64: return dispatch<64, 64, 1, 2, true>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 128:

@@ -11,6 +11,13 @@ namespace fa {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream);
 
+// Short sequences (bf16, 1 <= N <= 128, d in {64, 128}): the whole key/value range of a head in
+// one workgroup's LDS; same arguments as launch_fwd_bf16. short_fwd_applies: whether it takes
+// the problem.
+bool short_fwd_applies(int N, int d);
+hipError_t launch_fwd_short_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
+                                 float scale, bool causal, hipStream_t stream);
+
 // Grouped heads, sliding window, packed sequences (bf16, d in {64, 128}). Without cu_seqlens:
 // q, o [B, Hq, N, d], k, v [B, Hkv, N, d], lse [B, Hq, N]. With cu_seqlens (device int32, B + 1
 // offsets into N tokens): q, o [Hq, N, d], k, v [Hkv, N, d], lse [Hq, N], every sequence at most

@@ -93,4 +93,35 @@ __device__ __forceinline__ void load_resident(bf16x8 (&f)[D / 16], const bf16_t*
     for (int s = 0; s < D / 16; ++s) f[s] = ok ? *(const bf16x8*)(p + 16 * s) : bf16x8{};
 }
 
+// Write a wave's transposed fp32 accumulator (lane = row col, register 4a+b of d tile e =
+// column 32e + 8a + 4h + b) as bf16 rows times `mult`, staged through the wave's LDS tile
+// `stg` (32 x d) so that the global stores are whole rows, 16 bytes per lane.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mult, uint8_t* stg, bf16_t* out,
+                                           int row0, int N, int lane) {
+    using C = TileCfg<D>;
+    const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            bf16x4 ov;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ov[b] = (bf16_t)(acc[e][4 * a + b] * mult);
+            *(bf16x4*)(stg + col * C::ROW + 16 * ((4 * e + a) ^ (col & C::SWZ)) + 8 * h) = ov;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave reads back what its lanes wrote
+    __builtin_amdgcn_wave_barrier();
+    constexpr int LPR = C::ROW / 16, RPI = kWave / LPR;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = RPI * it + lane / LPR;
+        const int c = lane % LPR;
+        const i32x4 v = *(const i32x4*)(stg + r * C::ROW + 16 * (c ^ (r & C::SWZ)));
+        if (row0 + r < N) *(i32x4*)((uint8_t*)(out + (size_t)(row0 + r) * D) + 16 * c) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace fa
