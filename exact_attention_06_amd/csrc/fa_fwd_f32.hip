@@ -173,16 +173,18 @@ __global__ __launch_bounds__(kThreads, MINB) void fwd_f32_kernel(
 }
 
 // Small problems (fewer 128-query blocks than compute units): 32 queries per workgroup, the
-// key blocks dealt round-robin to its 4 waves, each with its own tiles (synchronised within
+// key blocks dealt round-robin to its W waves (8 at d = 64, 4 at d = 128, as the LDS allows),
+// each with its own tiles (synchronised within
 // the wave only) and its own online-softmax state; the four states are then combined in LDS
 // with the online-softmax merge ("FlashAttention-3 & GPU Kernel Optimization", section
 // "Online softmax tiling mathematics"): m = max m_w, O = sum 2^(m_w - m) O~_w / sum
-// 2^(m_w - m) l_w. A wave thus walks a quarter of the keys, which is what bounds these
+// 2^(m_w - m) l_w. A wave thus walks 1/W of the keys, which is what bounds these
 // latency-bound launches.
-constexpr int kSplitWaves = 4;
+template <int D>
+constexpr int split_waves() { return D <= 64 ? 8 : 4; }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_f32_split_kernel(
+template <int D, bool CAUSAL, int kSplitWaves = split_waves<D>()>
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void fwd_f32_split_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V, float* __restrict__ O,
     float* __restrict__ LSE, int N, int numQT, float c2) {
     constexpr int KP = D + 4;
@@ -350,7 +352,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float scale,
                         hipStream_t stream) {
     const int numQT = (N + 31) / 32;
-    hipLaunchKernelGGL((fwd_f32_split_kernel<D, CAUSAL>), dim3((unsigned)(BH * numQT)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_f32_split_kernel<D, CAUSAL>), dim3((unsigned)(BH * numQT)), dim3(64 * split_waves<D>()), 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, numQT, scale * kLog2e);
     return hipGetLastError();
 }
