@@ -57,6 +57,9 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, window, lengths or None)
     (1, 16, 4, 2048, 128, False, (-1, -1), (300, 1000, 748)),
     (1, 4, 2, 1500, 128, True, (64, 0), (5, 0, 700, 31, 764)),  # window + packing, empty and tiny sequences
     (1, 4, 2, 1000, 64, False, (20, 20), (1, 999)),
+    # N >= 4096 without packing takes the 256-query (8-wave) workgroups; ragged last block
+    (1, 4, 2, 4100, 128, False, (300, 200), None),
+    (1, 2, 1, 4100, 128, True, (-1, -1), None),
 ]
 
 
