@@ -20,6 +20,13 @@
 //    in registers and streams 32- or 64-query blocks of Q and dO through LDS. S = Q K^T and
 //    dP = dO V^T put one key in each lane pair; P and dS (bf16) are the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T from the LDS transpose read.
+//    At d = 128 the same work runs in bwd_dkdv_pair_kernel: 8 waves in pairs, one of each
+//    pair holding K (S, P, dV) and the other V (dP, dS, dK), P passed through LDS.
+//
+// Every step loop issues the next tiles' loads at its top and waits for them only at its end
+// (row values are loaded a step ahead, tile slots are separate LDS objects); causal waves or
+// pairs work only on the blocks their own rows reach and take part in the rest of the
+// workgroup's loads and barriers.
 //
 // MFMA layouts as in fa_common.h. The rows of the A operand of S / S^T are fed in the order
 // swap_bits23, so that result registers 8u .. 8u+7 of lane half h hold rows 16u + 8h + 0..7:

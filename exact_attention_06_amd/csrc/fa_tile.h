@@ -1,7 +1,8 @@
 // Row-major bf16 tiles of 32 (or 64) rows streamed into LDS by direct-to-LDS buffer loads,
 // with the per-lane addresses of the two ways the MFMA kernels read them: as A-operand rows
-// (d contiguous) and through the transposing read (rows contiguous). Shared by the backward
-// and the split-KV decoding kernels.
+// (d contiguous) and through the transposing read (rows contiguous), and the write-back of a
+// wave's transposed accumulator. Shared by the backward, the split-KV decoding and the
+// short-sequence forward kernels.
 #pragma once
 #include "fa_common.h"
 
