@@ -68,7 +68,7 @@ hipError_t dispatch_ext(const void* q, const void* k, const void* v, void* o, fl
 hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                int Hkv, int N, int max_seqlen, int d, float scale, bool causal, int left, int right,
                                const int* cu_seqlens, hipStream_t stream) {
-    const FwdExt ext{Hq, Hq / Hkv, left < 0 ? -1 : left, right < 0 ? -1 : right, N, cu_seqlens};
+    const FwdExt ext{Hq, Hq / Hkv, left < 0 ? -1 : left, right < 0 ? -1 : right, N, cu_seqlens, B};
     const int BH = B * Hq;
     const int Ngrid = cu_seqlens != nullptr ? max_seqlen : N;
     switch (d) {

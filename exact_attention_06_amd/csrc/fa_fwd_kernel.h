@@ -116,11 +116,91 @@ using IC = std::integral_constant<int, V>;
 // (a negative bound: no limit; the causal mask sets right = 0). With cu (cu[s], cu[s+1] the
 // token range of sequence s; the batch dimension is then 1) positions count from the start of
 // the sequence and keys of other sequences are never visited. ntot: tokens per (batch, head)
-// row of the tensors (N, or the total of the packed sequences).
+// row of the tensors (N, or the total of the packed sequences); nseq: the number of packed
+// sequences (with cu).
 struct FwdExt {
     int Hq, g, left, right, ntot;
     const int* cu;
+    int nseq;
 };
+
+// Query blocks of packed sequence s: ceil(rows / BR), at most numQB (the grid's longest
+// sequence); offsets clamped to [0, ntot] as where the kernel reads them.
+template <int BR>
+__device__ __forceinline__ int packed_blocks(const int* cu, int s, int ntot, int numQB) {
+    const int a = min(max(cu[s], 0), ntot);
+    const int n = min(max(cu[s + 1], a), ntot) - a;
+    return min((n + BR - 1) / BR, numQB);
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// index of the k-th set bit (k < popcount(m)) of a wave-uniform 64-bit mask
+__device__ __forceinline__ int kth_set_bit(uint64_t m, int k, int lane) {
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    return __ffsll((long long)__builtin_amdgcn_ballot_w64(((m >> lane) & 1) != 0 && rank == k)) - 1;
+}
+
+// Packed sequences: the grid enumerates only query blocks that exist (a grid of every sequence
+// times the longest one's blocks leaves most workgroups empty, and the hardware's dispatch order
+// then places the live ones on a fraction of the CUs). Work item r is block rank r / Hq, head
+// r % Hq; blocks are ranked by block index, highest first (for the causal mask the costliest
+// ones), then by sequence. Every lane takes part; the results are wave-uniform. Returns false
+// past the last block.
+template <int BR>
+__device__ bool packed_item(const FwdExt& ext, int numQB, int r, int lane, int& seq, int& hq, int& qb) {
+    const int rb = r / ext.Hq;
+    hq = r - rb * ext.Hq;
+    if (ext.nseq <= kWave) {
+        // one sequence per lane: walk the block levels down from the top, counting the
+        // sequences that have a block at each level (a ballot per level)
+        const int nb = lane < ext.nseq ? packed_blocks<BR>(ext.cu, lane, ext.ntot, numQB) : 0;
+        int above = 0;   // blocks ranked before level l
+        for (int l = numQB - 1; l >= 0; --l) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(nb > l);
+            const int c = __popcll(m);
+            if (rb < above + c) {
+                qb = l;
+                seq = kth_set_bit(m, rb - above, lane);
+                return true;
+            }
+            above += c;
+        }
+        return false;
+    }
+    // any number of sequences: blocks with an index above level l are
+    // sum over s of max(0, blocks(s) - l - 1); binary search for the level
+    auto above = [&](int l) {
+        int c = 0;
+        for (int s = lane; s < ext.nseq; s += kWave) c += max(0, packed_blocks<BR>(ext.cu, s, ext.ntot, numQB) - l - 1);
+        return wave_sum(c);
+    };
+    if (rb >= above(-1)) return false;
+    // the lowest level l with above(l) <= rb (above is non-increasing, above(numQB - 1) = 0)
+    int lo = 0, hi = numQB - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (above(mid) <= rb) hi = mid; else lo = mid + 1;
+    }
+    qb = lo;
+    // the k-th sequence (in order) that has block qb
+    int k = rb - above(qb);
+    for (int base = 0; base < ext.nseq; base += kWave) {
+        const int s = base + lane;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(s < ext.nseq && packed_blocks<BR>(ext.cu, s, ext.ntot, numQB) > qb);
+        const int c = __popcll(m);
+        if (k < c) {
+            seq = base + kth_set_bit(m, k, lane);
+            return true;
+        }
+        k -= c;
+    }
+    return false;   // not reached for consistent counts
+}
 
 // WAVES: waves per workgroup (each owns 32 NQ queries; all share the K/V tiles).
 // NQ: 32-query tiles per wave (the workgroup owns WAVES * 32 * NQ queries). With NQ = 2 every K
@@ -173,12 +253,14 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 
     int bh, qi;
     if (EXT && ext.cu != nullptr) {
-        // packed sequences of unequal lengths: query-block index major, so that the costliest
-        // blocks of every sequence and head are dispatched first and spread over all XCDs (the
-        // contiguous per-XCD ranges of the remap would put a long sequence on one or two XCDs)
-        const int rows = gridDim.x / numQB;
-        qi = blockIdx.x / rows;
-        bh = blockIdx.x - qi * rows;
+        // packed sequences of unequal lengths: the costliest blocks of every sequence and head
+        // are dispatched first and spread over all XCDs (the contiguous per-XCD ranges of the
+        // remap would put a long sequence on one or two XCDs)
+        int seq, hq, qbk;
+        if (!packed_item<BR>(ext, numQB, blockIdx.x, lane, seq, hq, qbk)) return;
+        bh = __builtin_amdgcn_readfirstlane(seq * ext.Hq + hq);
+        qbk = __builtin_amdgcn_readfirstlane(qbk);
+        qi = CAUSAL ? numQB - 1 - qbk : qbk;
     } else {
         // causal: each XCD's range ordered by query block first (costliest blocks first)
         work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL, bh, qi);
@@ -755,7 +837,11 @@ hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const 
     constexpr int BR = WAVES / DSPLIT * 32 * NQ;
     const int numQB = (N + BR - 1) / BR;
     const int nsb = (N + 63) / 64;
-    const long long total = (long long)BH * numQB;
+    long long total = (long long)BH * numQB;
+    // packed sequences: at most sum over s of ceil(n_s / BR) <= (ntot + nseq (BR - 1)) / BR
+    // blocks per head (the extra workgroups of a loose bound return at once)
+    if (EXT && ext.cu != nullptr)
+        total = std::min(total, (long long)ext.Hq * (((long long)ext.ntot + (long long)ext.nseq * (BR - 1)) / BR));
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT, DSPLIT>), dim3((unsigned)total),
                        dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e, ext);

@@ -45,6 +45,14 @@ def run(q, k, v, causal, window, cu=None):
     return o, lse
 
 
+def _many(count, seed):
+    # seeded document lengths, empty and single-token documents included
+    return tuple(int(x) for x in np.random.default_rng(seed).choice([0, 1, 9, 31, 64, 100, 130, 257], size=count))
+
+
+# more documents than a wave has lanes (64) take the kernel's general block enumeration
+_M64, _M65, _M90 = _many(64, 3), _many(65, 4), _many(90, 5)
+
 CASES = [  # (B, Hq, Hkv, N, d, causal, window, lengths or None)
     (2, 8, 2, 300, 128, False, (-1, -1), None),          # grouped heads only
     (2, 8, 2, 300, 128, True, (-1, -1), None),
@@ -60,6 +68,10 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, window, lengths or None)
     # N >= 4096 without packing takes the 256-query (8-wave) workgroups; ragged last block
     (1, 4, 2, 4100, 128, False, (300, 200), None),
     (1, 2, 1, 4100, 128, True, (-1, -1), None),
+    (1, 2, 1, sum(_M64), 128, True, (-1, -1), _M64),
+    (1, 2, 1, sum(_M65), 128, True, (-1, -1), _M65),
+    (1, 2, 1, sum(_M90), 128, False, (-1, -1), _M90),
+    (1, 4, 2, sum(_M90), 64, True, (40, 0), _M90),
 ]
 
 
