@@ -267,8 +267,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(
 
 // Combine the splits' states of every output row (page-5 merge), one wave per row:
 // M = max m_s, O = sum_s 2^(m_s - M) O~_s / sum_s 2^(m_s - M) l_s, LSE = (M + log2 l) ln 2.
-// Lane s fetches split s's (m, l) (nsplit <= 64); the O~ rows are then read with the lanes
-// along d, several splits' loads in flight at once.
+// Lane s fetches split s's (m, l) (nsplit <= 64); the O~ rows are read with the lanes along
+// d, several splits' loads in flight at once.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, bf16_t* __restrict__ O,
@@ -285,6 +285,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     const int rgi = rr / Nq, rqi = rr - rgi * Nq;
     const size_t orow = (size_t)(b * Hq + hkv * g + rgi) * Nq + rqi;
     const size_t p0 = (size_t)bkv * nsplit * R + rr;   // row of split s: p0 + s R
+    // the first splits' O~ rows are requested together with the (m, l) pairs: the merge then
+    // waits for one round trip to memory, not one per dependent step
+    constexpr int PRE = 4;
+    const float* src = part_o + p0 * D + lane * DPL;
+    float xp[PRE][DPL];
+#pragma unroll
+    for (int u = 0; u < PRE; ++u)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) xp[u][j] = u < nsplit ? src[(size_t)u * R * D + j] : 0.f;
     const bool have = lane < nsplit;
     const float ms = have ? part_ml[(p0 + (size_t)lane * R) * 2] : kDecSentinel;
     const float ls = have ? part_ml[(p0 + (size_t)lane * R) * 2 + 1] : 0.f;
@@ -296,8 +305,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 #pragma unroll
     for (int k = 32; k >= 1; k >>= 1) L += __shfl_xor(L, k);
     float o[DPL] = {};
-    const float* src = part_o + p0 * D + lane * DPL;
-    int s = 0;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const float ws = __shfl(w, u);   // 0 past nsplit (those lanes hold l = 0)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] = __builtin_fmaf(ws, xp[u][j], o[j]);
+    }
+    int s = PRE;
     for (; s + 4 <= nsplit; s += 4) {
         float x[4][DPL];
 #pragma unroll
