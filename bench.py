@@ -53,6 +53,7 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0         # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
 HEADLINE = "b4h16n8k_d128"
+EXT_BENCH = ("gqa_b2_hq16_hkv4_n8k_d128_causal", "swa_b2_hq16_hkv4_n8k_d128_w4096", "varlen_16docs_hq16_hkv4_n16k_d128")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd_bf16_b4h16n8k_d128.txt")
 
 
@@ -67,6 +68,7 @@ def parse_args():
     p.add_argument("--only-bwd", action="store_true")
     p.add_argument("--only-decode", action="store_true")
     p.add_argument("--only", default=None, help="fp8, or a forward workload name")
+    p.add_argument("--only-ext", default=None, help="one grouped-head / window / packed workload")
     return p.parse_args()
 
 
@@ -265,6 +267,35 @@ def main():
         return {"ms": round(m, 4), "bytes": nb, "GB/s": round(nb / m / 1e6, 1),
                 "frac_of_8TBs": round(nb / m / 1e6 / PEAK_HBM_GBS, 4)}
 
+    def ext_case(name, steps, warmup, ramp_ms):
+        # grouped heads / sliding window / packed documents: FLOPs of the visible (query, key) pairs
+        from exact_attention_06_amd import fa_fwd_ext
+        from exact_attention_06_amd.workloads import EXT_WORKLOADS, make_ext_inputs
+        we = EXT_WORKLOADS[name]
+        q, k, v, cu = make_ext_inputs(we)
+        lens = [we.N] * we.B if cu is None else [int(x) for x in (cu[1:] - cu[:-1])]
+        pairs = sum(visible_pairs(n, we.causal, we.window[0], we.window[1]) for n in lens)
+        fl = 4.0 * we.d * we.Hq * pairs
+        q, k, v = q.cuda(), k.cuda(), v.cuda()
+        cud = None if cu is None else cu.cuda()
+        mx = we.N if cu is None else max(lens)
+        o = torch.empty_like(q)
+        lse = torch.empty((we.B, we.Hq, we.N), dtype=torch.float32, device="cuda")
+        m = time_launches(torch, lambda: fa_fwd_ext(q, k, v, o, lse, causal=we.causal, window=we.window,
+                                                    cu_seqlens=cud, max_seqlen=mx), steps, warmup, ramp_ms)
+        progress(f"{name}: {m:.3f} ms, {fl / m / 1e9:.1f} TFLOP/s")
+        return {"ms": round(m, 4), "TFLOP/s": round(fl / m / 1e9, 1), "visible_pairs_per_head": pairs}
+
+    if args.only_ext is not None:
+        if args.only_ext not in EXT_BENCH:
+            print(f"--only-ext: one of {list(EXT_BENCH)}", file=sys.stderr)
+            return 2
+        r = ext_case(args.only_ext, args.steps, args.warmup, 100.0)
+        print(json.dumps({"metric": "attention fwd TFLOP/s over visible pairs (4*d each)", "value": r["TFLOP/s"],
+                          "unit": "TFLOP/s", "ms_per_step": r["ms"], "steps": args.steps,
+                          "config": {"workload": args.only_ext}}))
+        return 0
+
     if args.only_decode:
         from exact_attention_06_amd.workloads import DECODE_WORKLOADS
         wd = DECODE_WORKLOADS["decode_b16_hq32_hkv8_nk8k_d128"]
@@ -422,25 +453,8 @@ def main():
         from exact_attention_06_amd.workloads import DECODE_WORKLOADS
         for name in ("decode_b16_hq32_hkv8_nk8k_d128", "decode_b2_h32_nk32k_d128"):
             extra[name] = decode_case(DECODE_WORKLOADS[name], args.steps, args.warmup, 100.0)
-        from exact_attention_06_amd import fa_fwd_ext
-        from exact_attention_06_amd.workloads import EXT_WORKLOADS, make_ext_inputs
-        for name in ("gqa_b2_hq16_hkv4_n8k_d128_causal", "swa_b2_hq16_hkv4_n8k_d128_w4096",
-                     "varlen_16docs_hq16_hkv4_n16k_d128"):
-            we = EXT_WORKLOADS[name]
-            q, k, v, cu = make_ext_inputs(we)
-            lens = [we.N] * we.B if cu is None else [int(x) for x in (cu[1:] - cu[:-1])]
-            pairs = sum(visible_pairs(n, we.causal, we.window[0], we.window[1]) for n in lens)
-            fl = 4.0 * we.d * we.Hq * pairs
-            q, k, v = q.cuda(), k.cuda(), v.cuda()
-            cud = None if cu is None else cu.cuda()
-            mx = we.N if cu is None else max(lens)
-            o = torch.empty_like(q)
-            lse = torch.empty((we.B, we.Hq, we.N), dtype=torch.float32, device="cuda")
-            m = time_launches(torch, lambda: fa_fwd_ext(q, k, v, o, lse, causal=we.causal, window=we.window,
-                                                        cu_seqlens=cud, max_seqlen=mx), s2, w2, 100.0)
-            extra[name] = {"ms": round(m, 4), "TFLOP/s": round(fl / m / 1e9, 1), "visible_pairs_per_head": pairs}
-            progress(f"{name}: {m:.3f} ms, {fl / m / 1e9:.1f} TFLOP/s")
-            del q, k, v, o, lse
+        for name in EXT_BENCH:
+            extra[name] = ext_case(name, s2, w2, 100.0)
         result["extra"] = extra
     # calibration GEMM (hipBLASLt via torch): what a plain bf16 GEMM sustains on this GPU now
     a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
