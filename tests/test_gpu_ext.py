@@ -124,3 +124,19 @@ def test_ext_packed_workloads_every_row(name):
     o, lse = run(q, k, v, w.causal, w.window, cu)
     o_ref, lse_ref = attention_ext_fp64(q, k, v, w.scale, w.causal, w.window, cu.numpy())
     check(name, o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_grid_with_a_loose_max_seqlen(causal):
+    # max_seqlen may exceed the longest sequence (up to N): the grid then has block levels that
+    # no sequence reaches, and the result is the same, bit for bit
+    q, k, v = inputs(1, 4, 2, 2048, 128, 9)
+    cu = torch.tensor([0, 300, 300, 1300, 2048], dtype=torch.int32).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    outs = []
+    for mx in (1000, 1001, 2048):
+        o, lse = fa_fwd_ext(qc, kc, vc, causal=causal, cu_seqlens=cu, max_seqlen=mx)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
