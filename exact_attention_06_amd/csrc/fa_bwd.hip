@@ -16,8 +16,8 @@
 //    of K and V through LDS. S^T = K Q^T and dP^T = V dO^T put one query in each lane pair;
 //    P^T = exp2(S^T c - L log2 e) and dS^T = P^T o (dP^T - D) stay in registers and are the B
 //    operand (bf16) of dQ^T += K^T dS^T, whose A operand K^T comes from the LDS transpose read.
-// 3. bwd_dkdv_kernel, parallel over 128-key blocks: each wave keeps K^T and V^T of its 32 keys
-//    in registers and streams 32- or 64-query blocks of Q and dO through LDS. S = Q K^T and
+// 3. bwd_dkdv_kernel (d = 64), parallel over 128-key blocks: each wave keeps K^T and V^T of
+//    its 32 keys in registers and streams 32-query blocks of Q and dO through LDS. S = Q K^T and
 //    dP = dO V^T put one key in each lane pair; P and dS (bf16) are the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T from the LDS transpose read.
 //    At d = 128 the same work runs in bwd_dkdv_pair_kernel: 8 waves in pairs, one of each
@@ -44,17 +44,9 @@ namespace {
 
 constexpr int kBwdThreads = 256;   // 4 waves
 constexpr int kBwdRows = 32;       // rows per streamed tile of the dq kernel (keys)
-#ifndef FA_DQ_WAVES
-#define FA_DQ_WAVES 4   // 8 (256 queries per K/V tile, d = 128): 7.25 vs 7.10 ms for the whole backward at 8k
-#endif
-#ifndef FA_DKDV_ROWS
-#define FA_DKDV_ROWS 64
-#endif
-// queries per step of the dkdv kernel: two 32-query tiles at d = 128 (one wave per SIMD: the
-// second tile's products overlap the first tile's softmax); one at d = 64 (two waves per SIMD,
-// whose registers two tiles would exceed)
-template <int D>
-constexpr int dkdv_rows() { return D <= 64 ? 32 : FA_DKDV_ROWS; }
+// waves of the dq kernel: 128 queries per workgroup, two workgroups per CU (256 queries per
+// workgroup measured 7.25 vs 7.10 ms for the whole backward at 8k)
+constexpr int kDqWaves = 4;
 
 // ------------------------------------------------------------------------------------------
 // -D = -rowsum(dO o O)
@@ -97,13 +89,13 @@ using BIC = std::integral_constant<int, V>;
 // ------------------------------------------------------------------------------------------
 // dQ: parallel over 128-query blocks
 // ------------------------------------------------------------------------------------------
-// WAVES: 4 (128 queries per workgroup, two workgroups per CU) or 8 (256 queries share every
-// K/V tile, one workgroup per CU)
-template <int D, bool CAUSAL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
+// 4 waves (128 queries per workgroup), two workgroups per CU
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     bf16_t* __restrict__ dQ, int N, int numQB, float c2 /* scale*log2(e) */, float scale) {
+    constexpr int WAVES = kDqWaves;
     using C = TileCfg<D, kBwdRows, WAVES>;
     constexpr int BR = 32 * WAVES;
     constexpr int BC = kBwdRows;
@@ -216,26 +208,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void bwd_dq_kernel(
         }
     }
 
-    // dQ = scale dQ~ (each wave stages its tile in one of the four tile buffers; with 8 waves
-    // in two rounds)
-    const int slot = wave & 3;
-    uint8_t* const stg = slot == 0 ? sK0 : slot == 1 ? sK1 : slot == 2 ? sV0 : sV1;
-    if (wave < 4) store_rows<D>(acc, scale, stg, dQ + head, q0w, N, lane);
-    if constexpr (WAVES > 4) {
-        __syncthreads();
-        if (wave >= 4) store_rows<D>(acc, scale, stg, dQ + head, q0w, N, lane);
-    }
+    // dQ = scale dQ~ (each wave stages its tile in one of the four tile buffers)
+    uint8_t* const stg = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
+    store_rows<D>(acc, scale, stg, dQ + head, q0w, N, lane);
 }
 
 // ------------------------------------------------------------------------------------------
 // dK, dV: parallel over 128-key blocks
 // ------------------------------------------------------------------------------------------
-// MODE: 1 = dV only, 2 = dK only, 3 = both (one pass; at d = 128 that needs one wave per SIMD)
-template <int D, bool CAUSAL, int BQ, int MODE>
-__global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void bwd_dkdv_kernel(
+// Both gradients in one pass, 32 queries per step (d = 64: two waves per SIMD fit both
+// accumulators; d = 128 takes the wave-pair kernel below)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ Dl,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int numKB, float c2, float scale) {
+    static_assert(D <= 64, "both accumulators of a wave fit two waves per SIMD only at d <= 64");
+    constexpr int BQ = 32;
     using C = TileCfg<D, BQ>;
     constexpr int BK = 128;
     constexpr int QT = BQ / 32;   // 32-query tiles per step
@@ -262,10 +251,9 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
     TileAddr<D, BQ> ta;
     ta.init(wave, lane);
 
-    constexpr bool DOV = (MODE & 1) != 0, DOK = (MODE & 2) != 0;
     bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
     load_resident<D>(kf, K + head, krow, N, h);
-    if constexpr (DOK) load_resident<D>(vf, V + head, krow, N, h);
+    load_resident<D>(vf, V + head, krow, N, h);
 
     const int nqb = (N + BQ - 1) / BQ;
     const int i0 = CAUSAL ? min(k0, N) / BQ : 0;   // queries before the first key see none of it
@@ -290,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
                 for (int v2 = 0; v2 < 2; ++v2) {
                     const int off = 4 * (i * BQ + 32 * tt + 16 * u + 8 * h + 4 * v2);
                     lq_n[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rL, off));
-                    if constexpr (DOK) dq_n[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
+                    dq_n[tt][2 * u + v2] = __builtin_bit_cast(f32x4, buffer_load16(rDl, off));
                 }
     };
 
@@ -304,7 +292,7 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 lq[tt][r] = lq_n[tt][r];
-                if constexpr (DOK) dq[tt][r] = dq_n[tt][r];
+                dq[tt][r] = dq_n[tt][r];
             }
         load_rows(i + 1);
         // the next tiles, issued here (left to itself the scheduler sinks the loads to the end
@@ -321,17 +309,12 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
         for (int tt = 0; tt < QT; ++tt) {
             s[tt] = f32x16{};
             // dP - D: the product starts from -D (register r of query tile tt: dq[tt][r / 4][r % 4])
-            if constexpr (DOK) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dp[tt][r] = dq[tt][r / 4][r % 4];
-            } else {
-                dp[tt] = f32x16{};
-            }
+            for (int r = 0; r < 16; ++r) dp[tt][r] = dq[tt][r / 4][r % 4];
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
                 s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sQ1 : sQ0), st, tt), kf[st], s[tt], 0, 0, 0);
-                if constexpr (DOK)
-                    dp[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sD1 : sD0), st, tt), vf[st], dp[tt], 0, 0, 0);
+                dp[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row_operand((B ? sD1 : sD0), st, tt), vf[st], dp[tt], 0, 0, 0);
             }
         }
 #pragma unroll
@@ -340,23 +323,21 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
             bf16x8 pf[2], dsf[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(__builtin_fmaf(s[tt][r], c2, lq[tt][r / 4][r % 4]));   // lq: -LSE log2 e
+                float p = fast_exp2(__builtin_fmaf(s[tt][r], c2, lq[tt][r / 4][r % 4]));   // lq: -LSE log2 e
                 if constexpr (MASK) {
                     const int q = q0 + 32 * tt + 16 * (r / 8) + 8 * h + (r % 8);
                     p = (q >= N || (CAUSAL && q < krow)) ? 0.f : p;
                 }
-                if constexpr (DOV) pf[r / 8][r % 8] = (bf16_t)p;
-                if constexpr (DOK) dsf[r / 8][r % 8] = (bf16_t)(p * dp[tt][r]);
+                pf[r / 8][r % 8] = (bf16_t)p;
+                dsf[r / 8][r % 8] = (bf16_t)(p * dp[tt][r]);
             }
             // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries of tile tt
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int e = 0; e < C::DT; ++e) {
-                    if constexpr (DOV)
-                        dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sD1 : sD0), e, 2 * tt + ch), pf[ch], dv[e], 0, 0, 0);
-                    if constexpr (DOK)
-                        dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sQ1 : sQ0), e, 2 * tt + ch), dsf[ch], dk[e], 0, 0, 0);
+                    dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sD1 : sD0), e, 2 * tt + ch), pf[ch], dv[e], 0, 0, 0);
+                    dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand((B ? sQ1 : sQ0), e, 2 * tt + ch), dsf[ch], dk[e], 0, 0, 0);
                 }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -406,8 +387,8 @@ __global__ __launch_bounds__(kBwdThreads, (MODE != 3 || D <= 64) ? 2 : 1) void b
 
     // dK = scale dK~, dV = dV~; each wave stages its 32-key tile in one of the tile buffers
     uint8_t* const stg = wave == 0 ? sQ0 : wave == 1 ? sQ1 : wave == 2 ? sD0 : sD1;
-    if constexpr (DOK) store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
-    if constexpr (DOV) store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
+    store_rows<D>(dk, scale, stg, dK + head, k0w, N, lane);
+    store_rows<D>(dv, 1.f, stg, dV + head, k0w, N, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -651,35 +632,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     store_rows<D>(acc, pwave ? 1.f : scale, stg, (pwave ? dV : dK) + head, k0w, N, lane);
 }
 
-// dK and dV: one pass at d = 64; at d = 128 the two accumulators need more registers than two
-// waves per SIMD leave, and one wave per SIMD leaves the matrix cores idle most of the time,
-// so dV and dK run as two passes (S is recomputed once more: 5 products instead of 4)
+// dK and dV: one pass per 128-key block; d = 64 in one wave per 32 keys (a wave pair's 8
+// products per step are too few to pay for the per-step barrier of 8 waves and the P
+// exchange: 2.89 vs 2.22 ms at B=8 H=16 N=4k), d = 128 in wave pairs
 template <int D, bool CAUSAL>
 void launch_dkdv(const bf16_t* Qb, const bf16_t* Kb, const bf16_t* Vb, const bf16_t* dOb, const float* nl2,
                  const float* delta, bf16_t* dk, bf16_t* dv, int N, int nb, long long total, float c2, float scale,
                  hipStream_t stream) {
-#if defined(FA_BWD_SPLIT_DKDV)
-    constexpr int kind = D > 64 ? 2 : 0;
-#elif defined(FA_BWD_FUSED_DKDV)
-    constexpr int kind = 0;
-#elif defined(FA_BWD_PAIR_D64)
-    constexpr int kind = 1;
-#else
-    // d = 64: the fused kernel (a pair's 8 products per step are too few to pay for the
-    // per-step barrier of 8 waves and the P exchange: 2.89 vs 2.22 ms at B=8 H=16 N=4k)
-    constexpr int kind = D > 64 ? 1 : 0;
-#endif
-    if constexpr (kind == 1) {
+    if constexpr (D > 64) {
         hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(512), 0, stream, Qb, Kb, Vb,
                            dOb, nl2, delta, dk, dv, N, nb, c2, scale);
-    } else if constexpr (kind == 2) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 1>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
-                           Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 32, 2>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb,
-                           Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, dkdv_rows<D>(), 3>), dim3((unsigned)total), dim3(kBwdThreads), 0,
-                           stream, Qb, Kb, Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(kBwdThreads), 0, stream, Qb, Kb,
+                           Vb, dOb, nl2, delta, dk, dv, N, nb, c2, scale);
     }
 }
 
@@ -702,17 +667,16 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     const long long total = (long long)BH * nb;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     const bf16_t *Qb = (const bf16_t*)q, *Kb = (const bf16_t*)k, *Vb = (const bf16_t*)v, *dOb = (const bf16_t*)dout;
-    // dQ: 8 waves per workgroup where a 32-row tile has a load region for each of them
-    constexpr int DQW = (TileCfg<D, kBwdRows, 1>::TB / 1024 >= FA_DQ_WAVES) ? FA_DQ_WAVES : 4;
+    constexpr int DQW = kDqWaves;
     const int nbq = (N + 32 * DQW - 1) / (32 * DQW);
     const long long totalq = (long long)BH * nbq;
     if (causal) {
         launch_dkdv<D, true>(Qb, Kb, Vb, dOb, delta + rows, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, total, c2, scale, stream);
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true, DQW>), dim3((unsigned)totalq), dim3(64 * DQW), 0, stream, Qb, Kb,
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)totalq), dim3(64 * DQW), 0, stream, Qb, Kb,
                            Vb, dOb, lse, delta, (bf16_t*)dq, N, nbq, c2, scale);
     } else {
         launch_dkdv<D, false>(Qb, Kb, Vb, dOb, delta + rows, delta, (bf16_t*)dk, (bf16_t*)dv, N, nb, total, c2, scale, stream);
-        hipLaunchKernelGGL((bwd_dq_kernel<D, false, DQW>), dim3((unsigned)totalq), dim3(64 * DQW), 0, stream, Qb, Kb,
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)totalq), dim3(64 * DQW), 0, stream, Qb, Kb,
                            Vb, dOb, lse, delta, (bf16_t*)dq, N, nbq, c2, scale);
     }
     return hipGetLastError();

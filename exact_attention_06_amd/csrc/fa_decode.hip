@@ -35,9 +35,8 @@
 namespace fa {
 namespace {
 
-#ifndef FA_DECODE_WG
-#define FA_DECODE_WG 256
-#endif
+// workgroups a decoding launch aims for (one resident per compute unit)
+constexpr int kDecTargetWG = 256;
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr float kDecSentinel = -1e30f;   // running max before any visible key (finite: exp2(x - m) stays defined)
@@ -344,9 +343,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     p.ncg = (int)((R + 31) / 32);
     p.ntiles = (Nk + 31) / 32;
     const long long groups = (long long)B * Hkv * p.ncg;
-    // about FA_DECODE_WG workgroups (one resident per compute unit: the K/V buffers take 128 KB
+    // about kDecTargetWG workgroups (one resident per compute unit: the K/V buffers take 128 KB
     // of LDS at d = 128), at least 8 tiles (2 per wave) per split, at most 64 splits
-    long long ns = groups > 0 ? (FA_DECODE_WG + groups - 1) / groups : 1;
+    long long ns = groups > 0 ? (kDecTargetWG + groups - 1) / groups : 1;
     long long most = p.ntiles / 8 > 1 ? p.ntiles / 8 : 1;
     most = most < 64 ? most : 64;
     ns = ns < 1 ? 1 : (ns > most ? most : ns);

@@ -147,16 +147,6 @@ hipError_t launch_prep(const float* x, void* x8, float* s, const float* signs, i
     return hipGetLastError();
 }
 
-#ifndef FA_F8_D128_NQ
-#define FA_F8_D128_NQ 1
-#endif
-#ifndef FA_F8_D128_BC
-#define FA_F8_D128_BC 32
-#endif
-#ifndef FA_F8_D128_MINB
-#define FA_F8_D128_MINB (FA_F8_D128_NQ == 2 ? 1 : 2)
-#endif
-
 template <int D, int BC, int NQ, int MINB, bool PIPE>
 hipError_t dispatch_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                         const float* sv, void* o, float* lse, int BH, int N, float scale, bool causal,
@@ -187,7 +177,7 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
     // registers, as for bf16); conditional rescale threshold 2^8
     switch (d) {
         case 64: return dispatch_fp8<64, 64, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
-        case 128: return dispatch_fp8<128, FA_F8_D128_BC, FA_F8_D128_NQ, FA_F8_D128_MINB, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        case 128: return dispatch_fp8<128, 32, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         case 256: return dispatch_fp8<256, 64, 1, 1, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         default: return hipErrorInvalidValue;
     }

@@ -19,25 +19,6 @@
 #include "fa_fwd_kernel.h"
 #include "fa_internal.h"
 
-#ifndef FA_D128_NQ
-#define FA_D128_NQ 1
-#endif
-#ifndef FA_D128_BC
-#define FA_D128_BC 32
-#endif
-#ifndef FA_D128_MINB
-#define FA_D128_MINB (FA_D128_NQ == 2 ? 1 : 2)
-#endif
-#ifndef FA_D128_PIPE
-#define FA_D128_PIPE 1
-#endif
-#ifndef FA_SHORT
-#define FA_SHORT 1
-#endif
-#ifndef FA_D256_SPLIT
-#define FA_D256_SPLIT 1
-#endif
-
 
 namespace fa {
 namespace {
@@ -68,7 +49,11 @@ hipError_t dispatch_ext(const void* q, const void* k, const void* v, void* o, fl
 hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                int Hkv, int N, int max_seqlen, int d, float scale, bool causal, int left, int right,
                                const int* cu_seqlens, hipStream_t stream) {
-    const FwdExt ext{Hq, Hq / Hkv, left < 0 ? -1 : left, right < 0 ? -1 : right, N, cu_seqlens, B};
+    // a bound of N or more (positions differ by at most N - 1, also within a packed sequence) is
+    // no limit: mapped to -1, so that the kernel's edge arithmetic (query + right, query - left)
+    // stays far inside the int range
+    const auto bound = [N](int x) { return (x < 0 || x >= N) ? -1 : x; };
+    const FwdExt ext{Hq, Hq / Hkv, bound(left), bound(right), N, cu_seqlens, B};
     const int BH = B * Hq;
     const int Ngrid = cu_seqlens != nullptr ? max_seqlen : N;
     switch (d) {
@@ -77,8 +62,8 @@ hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void
             // long rows without packing: 8 waves (256 queries) share each K/V tile (grouped-head
             // causal at 8k +3.4%); packed documents keep the smaller workgroups (8 waves: -8%)
             if (cu_seqlens == nullptr && N >= 4096)
-                return dispatch_ext<128, FA_D128_BC, 1, 1, 8>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
-            return dispatch_ext<128, FA_D128_BC, 1, FA_D128_MINB>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
+                return dispatch_ext<128, 32, 1, 1, 8>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
+            return dispatch_ext<128, 32, 1, 2>(q, k, v, o, lse, BH, Ngrid, scale, causal, ext, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -86,7 +71,7 @@ hipError_t launch_fwd_ext_bf16(const void* q, const void* k, const void* v, void
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            float scale, bool causal, hipStream_t stream) {
     // a whole head in one workgroup's LDS (fa_fwd_short.hip)
-    if (FA_SHORT && short_fwd_applies(N, d)) return launch_fwd_short_bf16(q, k, v, o, lse, BH, N, d, scale, causal, stream);
+    if (short_fwd_applies(N, d)) return launch_fwd_short_bf16(q, k, v, o, lse, BH, N, d, scale, causal, stream);
     switch (d) {
         case 64: return dispatch<64, 64, 1, 2, true>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 128:
@@ -94,13 +79,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
             // which halves the tile traffic per FLOP (+3% at N = 8k); otherwise 4 waves, whose
             // smaller workgroups balance causal and short problems better
             if (!causal && N >= 2048)
-                return dispatch<128, FA_D128_BC, FA_D128_NQ, 1, FA_D128_PIPE != 0, 8>(q, k, v, o, lse, BH, N, scale,
-                                                                                    causal, stream);
-            return dispatch<128, FA_D128_BC, FA_D128_NQ, FA_D128_MINB, FA_D128_PIPE != 0, 4>(q, k, v, o, lse, BH, N, scale,
-                                                                                         causal, stream);
+                return dispatch<128, 32, 1, 1, true, 8>(q, k, v, o, lse, BH, N, scale, causal, stream);
+            return dispatch<128, 32, 1, 2, true, 4>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 256:
-            if (FA_D256_SPLIT) return dispatch<256, 32, 1, 1, true, 8, 2>(q, k, v, o, lse, BH, N, scale, causal, stream);
-            return dispatch<256, 32, 1, 1, false>(q, k, v, o, lse, BH, N, scale, causal, stream);
+            return dispatch<256, 32, 1, 1, true, 8, 2>(q, k, v, o, lse, BH, N, scale, causal, stream);
         default: return hipErrorInvalidValue;
     }
 }

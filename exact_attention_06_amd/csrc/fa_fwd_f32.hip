@@ -23,9 +23,6 @@ constexpr int kBR = 128;
 constexpr int kThreads = 256;
 constexpr int kBC = 32;   // keys per block
 constexpr int kSmallGrid = 256;   // one workgroup per compute unit
-#ifndef FA_F32_SPLIT
-#define FA_F32_SPLIT 1
-#endif
 
 template <int D, bool CAUSAL, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void fwd_f32_kernel(
@@ -373,7 +370,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           float scale, bool causal, hipStream_t stream) {
     // fewer 128-query blocks than compute units: split each block's keys over its waves
-    if (FA_F32_SPLIT && d <= 128 && (long long)BH * ((N + kBR - 1) / kBR) < kSmallGrid) {
+    if (d <= 128 && (long long)BH * ((N + kBR - 1) / kBR) < kSmallGrid) {
         if (d == 64) return causal ? launch_split<64, true>(q, k, v, o, lse, BH, N, scale, stream)
                                    : launch_split<64, false>(q, k, v, o, lse, BH, N, scale, stream);
         return causal ? launch_split<128, true>(q, k, v, o, lse, BH, N, scale, stream)

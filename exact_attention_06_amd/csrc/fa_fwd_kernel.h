@@ -649,7 +649,13 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             inv_r = svmax * __builtin_amdgcn_rcpf(sv);
         }
         const float ks = kscale(j);
+        // the wave's last block under a causal mask or a window's right edge holds its diagonal:
+        // the first rows of a head see only a few keys there, and rounding P to bf16 would cost
+        // up to 2^-9 of the largest value's magnitude. There P is carried as P_hi + P_lo (two
+        // bf16 terms, 2^-17 relative) and the block takes two PV products.
+        constexpr bool SPLITP = PER_WAVE && !NEXT;
         bf16x8 pf[NQ][C::CH];
+        bf16x8 plo[SPLITP ? NQ : 1][SPLITP ? C::CH : 1];
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
             const float ct = cq[n] * ks;
@@ -664,7 +670,9 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                     // fp32 P: the logsumexp needs the unrounded sum (started at the first term,
                     // not at 0, which would cost an add)
                     lsum = (t == 0 && i == 0) ? p : lsum + p;
-                    pf[n][2 * t + i / 8][i % 8] = (bf16_t)p;
+                    const bf16_t ph = (bf16_t)p;
+                    pf[n][2 * t + i / 8][i % 8] = ph;
+                    if constexpr (SPLITP) plo[n][2 * t + i / 8][i % 8] = (bf16_t)(p - (float)ph);   // p - ph is exact
                 }
             if constexpr (C::F8) lsum *= inv_r;
             l_run[n] += lsum;
@@ -684,8 +692,11 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 // concatenated as whole vectors (element-wise assembly is mis-compiled)
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                for (int n = 0; n < NQ; ++n)
+                for (int n = 0; n < NQ; ++n) {
                     acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[n][ch], acc[n][e], 0, 0, 0);
+                    if constexpr (SPLITP)
+                        acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, plo[n][ch], acc[n][e], 0, 0, 0);
+                }
             }
         // ---- mask and row max of block j+1 (d split: at the start of step j+1, after the exchange)
         if constexpr (PIPE && NEXT && DSPLIT == 1) {

@@ -93,18 +93,26 @@ __global__ __launch_bounds__(256, 2) void fwd_short_kernel(const bf16_t* __restr
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         if (j < nkw) {
-            bf16x8 pf[2];
+            // causal: the first rows see only a few keys, where rounding P to bf16 would cost up to
+            // 2^-9 of the largest value's magnitude; P is carried as P_hi + P_lo (two bf16 terms)
+            // and each block takes two PV products (the kernel is bound by memory, not MFMA)
+            bf16x8 pf[2], plo[CAUSAL ? 2 : 1];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p = fast_exp2(__builtin_fmaf(st[j][i], c2, -m2));
                 lsum += p;
-                pf[i / 8][i % 8] = (bf16_t)p;
+                const bf16_t ph = (bf16_t)p;
+                pf[i / 8][i % 8] = ph;
+                if constexpr (CAUSAL) plo[i / 8][i % 8] = (bf16_t)(p - (float)ph);   // p - ph is exact
             }
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-                for (int e = 0; e < C::DT; ++e)
-                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr_operand(sV + j * C::TB, e, ch), pf[ch], acc[e], 0, 0, 0);
+                for (int e = 0; e < C::DT; ++e) {
+                    const bf16x8 a = ta.tr_operand(sV + j * C::TB, e, ch);
+                    acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], acc[e], 0, 0, 0);
+                    if constexpr (CAUSAL) acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, plo[ch], acc[e], 0, 0, 0);
+                }
         }
     }
     const float l_tot = pair_sum(lsum);

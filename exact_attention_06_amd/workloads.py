@@ -14,6 +14,8 @@ below have the shapes, sizes and value distributions of the benchmark cases):
   then the random +-1 sign vector of the Hadamard rotation is drawn as
   ``where(torch.rand(d, generator=g) > 0.5, 1, -1)``. The signs are the only
   random numbers the method itself uses, so they are an input here.
+- Exact-rotation inputs of the FP8 quantiser's bit-level test: integers in [-8, 8] times 2^-2,
+  the same fraction of outliers times 20, then the signs (``make_fp8_exact_inputs``).
 - Backward workloads: the output gradient dO is the fourth iid N(0, 1) draw of the same
   generator (after Q, K, V), cast to bfloat16.
 - Decoding workloads: Q [B, Hq, Nq, d], then K and V [B, Hkv, Nk, d] (the key/value cache),
@@ -222,6 +224,21 @@ def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int):
         flat[idx] = flat[idx] * OUTLIER_FACTOR
     signs = torch.where(torch.rand(d, generator=g) > 0.5, 1.0, -1.0).to(torch.float32)
     return q, k, v, signs
+
+
+def make_fp8_exact_inputs(B: int, H: int, N: int, d: int, seed: int):
+    """Float32 x [B, H, N, d] whose Hadamard rotation is exact in float32 at d = 64 and 256, and
+    the +-1 signs [d]: x is an integer in [-8, 8] times 2^-2 (uniform), and floor(0.001 numel)
+    positions (randperm) are multiplied by 20 as in the FP8 workload. Every partial sum of the
+    transform is then a multiple of 2^-2 below 2^24 (exact), and 1/sqrt(d) is a power of two."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = (torch.randint(-8, 9, (B, H, N, d), generator=g).to(torch.float32) * 0.25).contiguous()
+    n_out = int(math.floor(OUTLIER_FRACTION * x.numel()))
+    idx = torch.randperm(x.numel(), generator=g)[:n_out]
+    flat = x.view(-1)
+    flat[idx] = flat[idx] * OUTLIER_FACTOR
+    signs = torch.where(torch.rand(d, generator=g) > 0.5, 1.0, -1.0).to(torch.float32)
+    return x, signs
 
 
 def make_inputs(w: Workload):

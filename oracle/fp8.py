@@ -100,11 +100,3 @@ def fp8_reference(q32, k32, v32, signs, scale: float, causal: bool, with_true: b
     if with_true:
         res["O_true"], res["LSE_true"] = attention_fp64(q32, k32, v32, scale, causal)
     return res
-
-
-def fp8_reference_rows(q8, k8, v8, sq, sk, sv, b: int, h: int, rows, scale: float, causal: bool):
-    """O_deq and LSE_deq for selected query rows of one (b, h), from codes and scales."""
-    qd = block_dequantize(q8[b, h], sq[b, h])
-    kd = block_dequantize(k8[b, h], sk[b, h])
-    vd = block_dequantize(v8[b, h], sv[b, h])
-    return attention_head_fp64(qd, kd, vd, scale, causal, rows=rows)

@@ -1,24 +1,25 @@
-"""Shared helpers for the GPU parity tests: tolerances and sampled oracle comparisons.
+"""Shared helpers for the GPU parity tests: the tolerances and whole-output comparisons.
 
-Tolerances (the contract for the floating-point outputs):
-- bf16 output O: |O_gpu - O_ref| <= 1e-2 + 2^-8 |O_ref| element-wise, and mean <= 1e-3
-  (for stress inputs outside the workloads whose |O| is near 1, the mean bound adds the
-  mean of half an ulp, 2^-9 |O_ref|: there rounding O alone costs ~8e-4 on average).
-  The 1e-2 is the contract; 2^-8 |O_ref| (one bf16 ulp of the reference value) is the
-  floor of a bf16 result: rounding O itself to bf16 costs up to half an ulp, and the
-  probability that multiplies the dominant value row is rounded to bf16 once before the
-  PV product (another half ulp on that term). It matters only where |O_ref| is large
-  (half an ulp is already 0.0156 for |O| in [4, 8)); the plain max |dO| is reported too;
-- LSE: |LSE_gpu - LSE_ref| <= 1e-4 * max(1, |LSE_ref|) (relative error, with an
-  absolute floor for rows whose LSE is near 0);
-- fp32 output (fp32 arithmetic throughout): max abs <= 2e-5, LSE as above with 1e-5.
-  fp32 rounding (2^-24 relative per operation) over sums of a few hundred terms of
-  magnitude <= 1 and the ~1-ulp hardware exp2 stay two orders of magnitude below this;
-- fp8 output O vs the oracle on the same (dequantised e4m3) inputs: |dO| <= 6e-2 + 2^-8 |O_ref|
-  (same floor as bf16: the output and the V values are rounded to bf16). Against the
-  original fp32 inputs no FP8 kernel can do this well on the outlier workload: attention
-  in exact arithmetic on the dequantised inputs is already 0.8 - 3 away from it (max abs),
-  so that error is reported, not bounded.
+Bounds for every parity case whose inputs are iid N(0, 1) (the five workloads, the headline
+and the smaller shapes and edge cases built the same way):
+- bf16 output O: max |O_gpu - O_ref| <= 1e-2 over every element, and mean <= 1e-3;
+- LSE: relative error |LSE_gpu - LSE_ref| / |LSE_ref| <= 1e-4 for every row (the
+  "max(1, |LSE_ref|)" form, an absolute floor of 1e-4 near LSE = 0, is printed beside it);
+- fp32 output (fp32 arithmetic throughout): max abs <= 2e-5, LSE relative 1e-5. fp32
+  rounding (2^-24 per operation) over sums of a few hundred terms of magnitude <= 1 and the
+  ~1-ulp hardware exp2 stay two orders of magnitude below this;
+- FP8 output O against attention on the same dequantised E4M3 inputs (O_deq): max abs
+  <= 6e-2 over every element; LSE against LSE_deq as above. Against the original fp32 inputs
+  (O_true) the error of any FP8 attention on the outlier workload is 0.8 - 3 (max abs: the
+  input quantisation alone moves the exact result that far), so that error is reported.
+
+Stress inputs outside the workloads (Q scaled by 8, so that a few keys dominate each row and
+|O| is near 1 on average) get one bf16 ulp of the reference added to the bound,
+|dO| <= 1e-2 + 2^-8 |O_ref| element-wise and mean <= 1e-3 + mean(2^-9 |O_ref|): rounding O to
+bf16 alone costs up to half an ulp, 8e-4 on average there. The plain figures are printed too.
+
+Outputs are pre-filled with NaN before each call, so a tile the kernels never write fails the
+comparison.
 """
 
 from __future__ import annotations
@@ -32,33 +33,123 @@ LSE_REL = 1e-4
 F32_MAX_ABS = 2e-5
 F32_LSE_REL = 1e-5
 FP8_MAX_ABS = 6e-2
-
-
-def to_np(t) -> np.ndarray:
-    return t.detach().to("cpu").to(torch.float64).numpy()
-
-
 BF16_ULP_REL = 2.0 ** -8
 
 
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_np(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64, copy=False)
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def nan_out(shape, dtype, device="cuda") -> torch.Tensor:
+    """An output tensor filled with NaN (a result the kernels never write stays NaN)."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype, device=device)
+
+
+def o_err(o_gpu, o_ref):
+    d = np.abs(to_np(o_gpu) - o_ref)
+    return (float(d.max()), float(d.mean())) if d.size else (0.0, 0.0)
+
+
 def o_excess(o_gpu, o_ref, tol_abs) -> float:
-    """max over elements of |dO| - (tol_abs + 2^-8 |O_ref|); <= 0 means within the bound."""
-    g = to_np(o_gpu) if not isinstance(o_gpu, np.ndarray) else o_gpu
+    """Stress inputs only: max over elements of |dO| - (tol_abs + 2^-8 |O_ref|) (<= 0: within)."""
+    g = to_np(o_gpu)
     if g.size == 0:
         return -tol_abs
     return float((np.abs(g - o_ref) - (tol_abs + BF16_ULP_REL * np.abs(o_ref))).max())
 
 
-def o_err(o_gpu, o_ref):
-    d = np.abs(to_np(o_gpu) - o_ref) if not isinstance(o_gpu, np.ndarray) else np.abs(o_gpu - o_ref)
-    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
-
-
 def lse_rel_err(lse_gpu, lse_ref) -> float:
-    g = to_np(lse_gpu) if not isinstance(lse_gpu, np.ndarray) else lse_gpu
+    """max |dLSE| / |LSE_ref| over rows (rows with LSE_ref = -inf, no visible key, must match)."""
+    g = to_np(lse_gpu)
     if g.size == 0:
         return 0.0
-    return float((np.abs(g - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
+    dead = ~np.isfinite(lse_ref)
+    if dead.any():
+        assert np.array_equal(g[dead], lse_ref[dead]), "rows without a visible key need LSE = -inf"
+    live = ~dead
+    if not live.any():
+        return 0.0
+    return float((np.abs(g[live] - lse_ref[live]) / np.abs(lse_ref[live])).max())
+
+
+def lse_floor_err(lse_gpu, lse_ref) -> float:
+    """max |dLSE| / max(1, |LSE_ref|) over rows with a visible key."""
+    g = to_np(lse_gpu)
+    live = np.isfinite(lse_ref)
+    if not live.any():
+        return 0.0
+    return float((np.abs(g[live] - lse_ref[live]) / np.maximum(1.0, np.abs(lse_ref[live]))).max())
+
+
+class Tally:
+    """Running figures of one whole-output comparison (max and mean |dO|, LSE errors)."""
+
+    def __init__(self, label: str):
+        self.label = label
+        self.max = 0.0
+        self.sum = 0.0
+        self.count = 0
+        self.lse_rel = 0.0
+        self.lse_floor = 0.0
+        self.where = None
+        self.ref_at_max = 0.0
+
+    def add(self, key, o_gpu, o_ref, lse_gpu=None, lse_ref=None):
+        g = to_np(o_gpu)
+        d = np.abs(g - o_ref)
+        if d.size:
+            i = int(np.argmax(d))
+            if d.flat[i] > self.max or self.where is None:
+                self.max = float(d.flat[i])
+                self.where = (key, np.unravel_index(i, d.shape))
+                self.ref_at_max = float(np.abs(o_ref).flat[i])
+            self.sum += float(d.sum())
+            self.count += d.size
+        if lse_ref is not None:
+            self.lse_rel = max(self.lse_rel, lse_rel_err(lse_gpu, lse_ref))
+            self.lse_floor = max(self.lse_floor, lse_floor_err(lse_gpu, lse_ref))
+
+    @property
+    def mean(self) -> float:
+        return self.sum / max(1, self.count)
+
+    def report(self):
+        say(f"  {self.label}: {self.count} elements, max|dO|={self.max:.4g} (at {self.where}, |O_ref|="
+            f"{self.ref_at_max:.3g}) mean|dO|={self.mean:.3g} LSE rel={self.lse_rel:.3g} "
+            f"(max(1,|LSE|) form {self.lse_floor:.3g})")
+
+    def check(self, max_abs=BF16_MAX_ABS, mean_abs=BF16_MEAN_ABS, lse_rel=LSE_REL):
+        self.report()
+        assert self.count > 0
+        assert self.max <= max_abs, f"{self.label}: max|dO| {self.max:.4g} > {max_abs}"
+        assert self.mean <= mean_abs, f"{self.label}: mean|dO| {self.mean:.4g} > {mean_abs}"
+        assert self.lse_rel <= lse_rel, f"{self.label}: LSE relative error {self.lse_rel:.3g} > {lse_rel}"
+
+
+def all_finite(*ts):
+    """Every element written (the outputs started as NaN) and finite."""
+    for t in ts:
+        if t is not None:
+            assert bool(torch.isfinite(t).all()), "an output element is NaN or infinite (not written?)"
+
+
+def compare_heads(o, lse, ref_head, heads, label: str) -> Tally:
+    """Compare o [.., N, d] and lse [.., N] (GPU) with ref_head(b, h) -> (O_ref, LSE_ref) for
+    every (b, h) in heads; returns the tally (not yet checked)."""
+    all_finite(o, lse)
+    oc = o.float().cpu()
+    lc = lse.cpu() if lse is not None else None
+    t = Tally(label)
+    for b, h in heads:
+        o_ref, lse_ref = ref_head(b, h)
+        t.add((b, h), oc[b, h], o_ref, None if lc is None else lc[b, h], None if lc is None else lse_ref)
+    return t
 
 
 def sample_rows(n: int, count: int, seed: int) -> np.ndarray:

@@ -1,12 +1,12 @@
 """GPU parity of split-key decoding (fa_decode) against the float64 decoding oracle, through
 the C ABI.
 
-Bounds: the forward's bf16 bounds (tests/_parity.py): |O_gpu - O_ref| <= 1e-2 + 2^-8 |O_ref|
-element-wise, mean <= 1e-3, and |LSE_gpu - LSE_ref| <= 1e-4 max(1, |LSE_ref|). The arithmetic is
+Bounds: the forward's bf16 bounds (tests/_parity.py): max |O_gpu - O_ref| <= 1e-2 and mean
+<= 1e-3 over every element, LSE relative error <= 1e-4. The arithmetic is
 the forward's (bf16 products, fp32 accumulation, P rounded to bf16 for the PV product, l summed
 from fp32 P); the merge of the splits' states adds a few fp32 roundings.
 Decoding outputs are small, so every case compares every output row with the oracle, the
-full-size workloads included.
+full-size workloads included; outputs start as NaN.
 """
 
 import numpy as np
@@ -16,7 +16,7 @@ import torch
 from exact_attention_06_amd import fa_decode, fa_decode_workspace_size, fa_fwd
 from exact_attention_06_amd.workloads import DECODE_WORKLOADS, make_decode_inputs, make_qkv
 from oracle.decode import attention_decode_fp64
-from tests._parity import BF16_MAX_ABS, BF16_MEAN_ABS, LSE_REL, lse_rel_err, o_err, o_excess, to_np
+from tests._parity import BF16_MAX_ABS, Tally, all_finite, nan_out, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -26,15 +26,16 @@ def say(*a):
 
 
 def check(name, o, lse, o_ref, lse_ref):
-    mx, mean = o_err(o, o_ref)
-    ex = o_excess(o, o_ref, BF16_MAX_ABS)
-    le = lse_rel_err(lse, lse_ref)
-    say(f"  {name}: max|dO|={mx:.3g} (excess {ex:.3g}) mean={mean:.3g} lse rel={le:.3g}")
-    assert ex <= 0 and mean <= BF16_MEAN_ABS and le <= LSE_REL, name
+    all_finite(o, lse)
+    t = Tally(name)
+    t.add(None, o.float().cpu(), o_ref, lse.cpu(), lse_ref)
+    t.check()
 
 
 def run(q, k, v, causal, ws=None):
-    o, lse = fa_decode(q.cuda(), k.cuda(), v.cuda(), workspace=ws, causal=causal)
+    o = nan_out(q.shape, torch.bfloat16)
+    lse = nan_out(q.shape[:3], torch.float32)
+    fa_decode(q.cuda(), k.cuda(), v.cuda(), o, lse, workspace=ws, causal=causal)
     torch.cuda.synchronize()
     return o, lse
 
@@ -87,7 +88,7 @@ def test_decode_equals_forward_when_lengths_match():
         o, lse = run(q, k, v, causal)
         of, lf = fa_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
         torch.cuda.synchronize()
-        assert float((o.float() - of.float()).abs().max()) <= 2 * BF16_MAX_ABS
+        assert float((o.float() - of.float()).abs().max()) <= 2 * BF16_MAX_ABS   # each within 1e-2 of the oracle
         assert float((lse - lf).abs().max()) <= 2e-4 * max(1.0, float(lf.abs().max()))
 
 

@@ -1,15 +1,20 @@
 """GPU parity of the FP8 path (fa_prep_fp8, fa_fwd_fp8) against the oracle, through the C ABI.
 
-- fa_prep_fp8 without rotation must reproduce the oracle's codes and scales bit for bit
-  (both sides compute amax, amax/448 and x/s in float32 and round to nearest even).
-- With rotation the GPU's float32 fast Walsh-Hadamard transform differs from the
-  oracle's float64 dense product by a few float32 ulps, so a code may differ where the
-  rotated value lies next to a rounding midpoint: codes must agree except for a tiny
-  fraction, and those must be neighbouring E4M3 values; scales agree to 1e-6.
-- fa_fwd_fp8 is fed the oracle's own codes and scales (no GPU-made input) and compared
-  with attention on the dequantised inputs (O_deq, LSE_deq): |dO| <= 6e-2 + 2^-8 |O_ref|
-  (tests/_parity.py) and LSE relative 1e-4. The error against the original float32
-  inputs (O_true) is reported: it is dominated by the input quantisation itself.
+- fa_prep_fp8 without rotation reproduces the oracle's codes and scales bit for bit (both
+  sides compute amax, amax/448 and x/s in float32 and round to nearest even).
+- With rotation, on inputs whose fast Walsh-Hadamard transform is exact in float32 (small
+  integers times a power of two, with outliers) at d = 64 and d = 256, where 1/sqrt(d) is a
+  power of two: the rotated values are then exact on both sides, and the GPU's codes and
+  scales equal the oracle's bit for bit. On general inputs the GPU's float32 transform differs
+  from the oracle's float64 product by a few float32 ulps, so a code may differ where the
+  rotated value lies next to a rounding midpoint: codes agree except for a tiny fraction, and
+  those are neighbouring E4M3 values; scales agree to 1e-6.
+- fa_fwd_fp8 is compared with attention on the dequantised inputs (O_deq, LSE_deq) over the
+  whole output: max |dO| <= 6e-2, mean <= 1e-3, LSE relative <= 1e-4. The FP8 workload is
+  checked twice at full size: on the oracle's codes, and through the GPU's own rotation and
+  quantisation (codes that may differ from the oracle's by one step on a few near-midpoint
+  values, so the bound covers that too). The error against the original float32 inputs
+  (O_true) is reported: it is dominated by the input quantisation itself.
 """
 
 import numpy as np
@@ -17,37 +22,64 @@ import pytest
 import torch
 
 from exact_attention_06_amd import fa_fwd_fp8, fa_prep_fp8
-from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_inputs
-from oracle.attention import attention_fp64, attention_head_fp64
+from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_exact_inputs, make_fp8_inputs
+from oracle.attention import attention_head_fp64
 from oracle.e4m3 import e4m3_decode
 from oracle.fp8 import block_dequantize, block_quantize, fp8_inputs, fp8_reference, rotate_to_f32
-from tests._parity import FP8_MAX_ABS, LSE_REL, lse_rel_err, o_err, o_excess, sample_rows, to_np
+from tests._parity import (BF16_MEAN_ABS, FP8_MAX_ABS, LSE_REL, Tally, all_finite, nan_out, o_err, say)
 
 pytestmark = pytest.mark.gpu
 
 
+def prep(x, signs=None):
+    B, H, N, d = x.shape
+    nsb = (N + 63) // 64
+    x8 = torch.full((B, H, N, d), 0x7F, dtype=torch.uint8, device="cuda")   # e4m3 NaN until written
+    s = nan_out((B, H, nsb), torch.float32)
+    fa_prep_fp8(x.cuda(), None if signs is None else signs.cuda(), x8, s)
+    torch.cuda.synchronize()
+    return x8, s
 
-def say(*a):
-    print(*a, flush=True)
+
+def fwd(q8, k8, v8, sq, sk, sv, causal=False):
+    B, H, N, d = q8.shape
+    o = nan_out((B, H, N, d), torch.bfloat16)
+    lse = nan_out((B, H, N), torch.float32)
+    fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, causal=causal)
+    torch.cuda.synchronize()
+    all_finite(o, lse)
+    return o, lse
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 200, 128), (2, 1, 64, 64), (1, 1, 130, 256)])
 def test_prep_without_rotation_is_bit_exact(shape):
     say(f"prep no-rotation {shape}")
     x, _, _, _ = make_fp8_inputs(*shape, seed=21)
-    x8, s = fa_prep_fp8(x.cuda())
-    torch.cuda.synchronize()
+    x8, s = prep(x)
     codes, scales = block_quantize(x.numpy())
     assert np.array_equal(s.cpu().numpy(), scales)
     assert np.array_equal(x8.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 200, 64), (1, 3, 130, 256), (1, 1, 64, 256), (1, 2, 1, 64)])
+def test_prep_with_rotation_is_bit_exact_on_exact_transforms(shape):
+    """Integer parity of the rotated quantiser: the rotation is exact on these inputs, so the
+    codes and scales depend only on the float32 amax / 448, x / s and the E4M3 rounding."""
+    say(f"prep rotation, exact transform {shape}")
+    x, signs = make_fp8_exact_inputs(*shape, seed=25)
+    x8, s = prep(x, signs)
+    codes, scales = block_quantize(rotate_to_f32(x.numpy(), signs.numpy()))
+    assert np.array_equal(s.cpu().numpy(), scales)
+    g = x8.cpu().numpy()
+    say(f"  codes differing: {int((g != codes).sum())} of {g.size}")
+    assert np.array_equal(g, codes)
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 200, 128), (2, 1, 64, 64), (1, 1, 130, 256)])
 def test_prep_with_rotation(shape):
     say(f"prep rotation {shape}")
     x, _, _, signs = make_fp8_inputs(*shape, seed=22)
-    x8, s = fa_prep_fp8(x.cuda(), signs.cuda())
-    torch.cuda.synchronize()
+    x8, s = prep(x, signs)
     codes, scales = block_quantize(rotate_to_f32(x.numpy(), signs.numpy()))
     np.testing.assert_allclose(s.cpu().numpy(), scales, rtol=1e-6)
     g = x8.cpu().numpy()
@@ -59,68 +91,73 @@ def test_prep_with_rotation(shape):
     assert (np.abs(dg - dr) <= step * 1.0001).all()
 
 
+def check_vs_deq(o, lse, o_deq, lse_deq, label, o_true=None):
+    t = Tally(label)
+    t.add(None, o.float().cpu(), o_deq, lse.cpu(), lse_deq)
+    if o_true is not None:
+        mt, _ = o_err(o.float().cpu(), o_true)
+        floor, _ = o_err(o_deq, o_true)
+        say(f"  vs O_true max={mt:.3g} (O_deq vs O_true {floor:.3g})")
+    t.check(FP8_MAX_ABS, BF16_MEAN_ABS, LSE_REL)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 300, 128), (2, 2, 128, 64), (1, 1, 200, 256), (1, 1, 1, 128)])
 def test_fwd_fp8_small(shape, causal):
     say(f"fwd fp8 {shape} causal={causal}")
     B, H, N, d = shape
     q, k, v, signs = make_fp8_inputs(B, H, N, d, seed=23 + N)
-    scale = 1.0 / np.sqrt(d)
-    ref = fp8_reference(q.numpy(), k.numpy(), v.numpy(), signs.numpy(), scale, causal)
+    ref = fp8_reference(q.numpy(), k.numpy(), v.numpy(), signs.numpy(), 1.0 / np.sqrt(d), causal)
     t = {n: torch.from_numpy(ref[n]).cuda() for n in ("q8", "k8", "v8", "sq", "sk", "sv")}
-    o, lse = fa_fwd_fp8(t["q8"], t["k8"], t["v8"], t["sq"], t["sk"], t["sv"], causal=causal)
-    torch.cuda.synchronize()
-    mx, mean = o_err(o, ref["O_deq"])
-    ex = o_excess(o, ref["O_deq"], FP8_MAX_ABS)
-    le = lse_rel_err(lse, ref["LSE_deq"])
-    mt, _ = o_err(o, ref["O_true"])
-    floor, _ = o_err(ref["O_deq"], ref["O_true"])
-    say(f"  vs O_deq max={mx:.3g} (excess {ex:.3g}) mean={mean:.3g} lse_rel={le:.3g}; "
-        f"vs O_true max={mt:.3g} (O_deq vs O_true {floor:.3g})")
-    assert ex <= 0 and le <= LSE_REL
+    o, lse = fwd(t["q8"], t["k8"], t["v8"], t["sq"], t["sk"], t["sv"], causal)
+    check_vs_deq(o, lse, ref["O_deq"], ref["LSE_deq"], f"fp8 {shape} causal={causal}", ref["O_true"])
 
 
 def test_fp8_end_to_end_small():
     say("fp8 end to end (prep on GPU, then fwd)")
     q, k, v, signs = make_fp8_inputs(2, 2, 512, 128, seed=24)
-    sd = signs.cuda()
-    q8, sq = fa_prep_fp8(q.cuda(), sd)
-    k8, sk = fa_prep_fp8(k.cuda(), sd)
-    v8, sv = fa_prep_fp8(v.cuda())
-    o, lse = fa_fwd_fp8(q8, k8, v8, sq, sk, sv)
-    torch.cuda.synchronize()
+    q8, sq = prep(q, signs)
+    k8, sk = prep(k, signs)
+    v8, sv = prep(v)
+    o, lse = fwd(q8, k8, v8, sq, sk, sv)
     ref = fp8_reference(q.numpy(), k.numpy(), v.numpy(), signs.numpy(), 1 / np.sqrt(128), False)
-    mx, mean = o_err(o, ref["O_deq"])
-    ex = o_excess(o, ref["O_deq"], FP8_MAX_ABS)
-    mt, _ = o_err(o, ref["O_true"])
-    say(f"  vs O_deq max={mx:.3g} (excess {ex:.3g}) mean={mean:.3g}; vs O_true max={mt:.3g}")
-    # the GPU quantiser may round a few near-tie values the other way than the oracle's
-    # (float32 vs float64 rotation), so the inputs differ slightly from the oracle's codes
-    assert ex <= 0
+    # the GPU quantiser may round a few near-midpoint values the other way than the oracle's
+    # (float32 vs float64 rotation), so its codes may differ from the oracle's by one step there
+    check_vs_deq(o, lse, ref["O_deq"], ref["LSE_deq"], "fp8 end to end", ref["O_true"])
 
 
-def test_fp8_workload_sampled():
+def test_fp8_workload_whole_output():
+    """The FP8 workload at full size, every element: the forward on the oracle's codes, and the
+    whole GPU chain (rotation and quantisation of Q, K, V on the GPU, then the forward)."""
     w = WORKLOADS["fp8_b4h16n8k_d128"]
-    say(f"workload {w.name} (sampled rows)")
+    say(f"workload {w.name} (whole output; oracle codes and the GPU's own)")
     q, k, v, signs = make_fp8_inputs(w.B, w.H, w.N, w.d, w.seed)
     qi = fp8_inputs(q.numpy(), k.numpy(), v.numpy(), signs.numpy())
     t = {n: torch.from_numpy(qi[n]).cuda() for n in ("q8", "k8", "v8", "sq", "sk", "sv")}
-    o, lse = fa_fwd_fp8(t["q8"], t["k8"], t["v8"], t["sq"], t["sk"], t["sv"])
-    torch.cuda.synchronize()
-    worst = [0.0, 0.0, 0.0, -1.0]
-    for b, h in [(0, 0), (1, 7), (3, 15)]:
-        rows = sample_rows(w.N, 96, seed=b * 100 + h)
-        qd = block_dequantize(qi["q8"][b, h], qi["sq"][b, h])
-        kd = block_dequantize(qi["k8"][b, h], qi["sk"][b, h])
-        vd = block_dequantize(qi["v8"][b, h], qi["sv"][b, h])
-        o_deq, lse_deq = attention_head_fp64(qd, kd, vd, w.scale, False, rows=rows)
-        o_true, _ = attention_head_fp64(q[b, h], k[b, h], v[b, h], w.scale, False, rows=rows)
-        idx = torch.from_numpy(rows).cuda()
-        og, lg = to_np(o[b, h][idx]), to_np(lse[b, h][idx])
-        worst[0] = max(worst[0], o_err(og, o_deq)[0])
-        worst[1] = max(worst[1], lse_rel_err(lg, lse_deq))
-        worst[2] = max(worst[2], o_err(og, o_true)[0])
-        worst[3] = max(worst[3], o_excess(og, o_deq, FP8_MAX_ABS))
-    say(f"  vs O_deq max={worst[0]:.3g} (excess {worst[3]:.3g}) lse_rel={worst[1]:.3g}; vs O_true max={worst[2]:.3g}")
-    assert worst[3] <= 0 and worst[1] <= LSE_REL
-    assert torch.isfinite(o.float()).all()
+    o1, l1 = fwd(t["q8"], t["k8"], t["v8"], t["sq"], t["sk"], t["sv"])
+    del t
+    q8, sq = prep(q, signs)
+    k8, sk = prep(k, signs)
+    v8, sv = prep(v)
+    o2, l2 = fwd(q8, k8, v8, sq, sk, sv)
+    ncode = sum(int((a.cpu().numpy() != qi[n]).sum()) for a, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")))
+    say(f"  GPU codes differing from the oracle's: {ncode} of {3 * q.numel()}")
+    del q8, k8, v8
+    o1c, l1c, o2c, l2c = o1.float().cpu(), l1.cpu(), o2.float().cpu(), l2.cpu()
+    t1, t2 = Tally(f"{w.name} on the oracle's codes"), Tally(f"{w.name} GPU prep -> GPU forward")
+    true_err, floor = 0.0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            qd = block_dequantize(qi["q8"][b, h], qi["sq"][b, h])
+            kd = block_dequantize(qi["k8"][b, h], qi["sk"][b, h])
+            vd = block_dequantize(qi["v8"][b, h], qi["sv"][b, h])
+            o_deq, lse_deq = attention_head_fp64(qd, kd, vd, w.scale, False)
+            t1.add((b, h), o1c[b, h], o_deq, l1c[b, h], lse_deq)
+            t2.add((b, h), o2c[b, h], o_deq, l2c[b, h], lse_deq)
+            if (b, h) in ((0, 0), (3, 15)):   # the original inputs' result, reported
+                o_true, _ = attention_head_fp64(q[b, h], k[b, h], v[b, h], w.scale, False)
+                true_err = max(true_err, o_err(o1c[b, h], o_true)[0])
+                floor = max(floor, o_err(o_deq, o_true)[0])
+    say(f"  heads (0,0), (3,15): vs O_true max={true_err:.3g} (O_deq vs O_true {floor:.3g})")
+    t1.check(FP8_MAX_ABS, BF16_MEAN_ABS, LSE_REL)
+    t2.check(FP8_MAX_ABS, BF16_MEAN_ABS, LSE_REL)

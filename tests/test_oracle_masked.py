@@ -2,8 +2,8 @@
 
 - with no window, no packing and one key/value head per query head it is the pinned forward
   oracle, causal and not;
-- the dense reference of Exercise 5 (FA2/3 page): torch softmax over the scores with the mask
-  "k <= q and k > q - w" equals the causal window (w - 1, 0);
+- the causal window of Exercise 5 (FA2/3 page), w keys ending at the query, computed row by
+  row from each row's own key range, equals the window (w - 1, 0);
 - closed forms: the window (0, 0) lets every query see only itself, so O = V and
   LSE_i = scale q_i . k_i; windows wider than the sequence change nothing;
 - a pure-Python brute force of a two-sided non-causal window on a tiny case;
@@ -19,7 +19,6 @@ import math
 
 import numpy as np
 import pytest
-import torch
 
 from oracle.attention import attention_fp64
 from oracle.masked import attention_ext_fp64, attention_ext_rows_fp64, visible_mask, visible_pairs
@@ -38,19 +37,24 @@ def test_plain_case_is_the_forward_oracle(causal):
 
 
 @pytest.mark.parametrize("w", [1, 7, 48, 200])
-def test_exercise5_dense_reference(w):
+def test_causal_window_of_w_keys_row_by_row(w):
+    """The sliding window of Exercise 5 on "FlashAttention 2 & 3: Work Partitioning, Warp
+    Specialization & FP8": query i sees the w keys max(0, i - w + 1) .. i. Each row is
+    computed on its own from that range alone (a softmax over just those scores, in float64,
+    with the logsumexp from math.fsum), which must equal the oracle's window (w - 1, 0)."""
     n, d = 96, 16
     q, k, v = _rand(4, n, d), _rand(5, n, d), _rand(6, n, d)
-    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
-    s = qt @ kt.T / math.sqrt(d)
-    i = torch.arange(n)[:, None]
-    j = torch.arange(n)[None, :]
-    allowed = (j <= i) & (j > i - w)
-    s = s.masked_fill(~allowed, float("-inf"))
-    ref = torch.softmax(s, dim=-1) @ vt
-    o, lse = attention_ext_fp64(q[None, None], k[None, None], v[None, None], 1 / math.sqrt(d), True, (w - 1, 0))
-    assert np.allclose(o[0, 0], ref.numpy(), rtol=0, atol=1e-13)
-    assert np.allclose(lse[0, 0], torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-13)
+    scale = 1 / math.sqrt(d)
+    o, lse = attention_ext_fp64(q[None, None], k[None, None], v[None, None], scale, True, (w - 1, 0))
+    for i in range(n):
+        keys = range(max(0, i - w + 1), i + 1)
+        scores = [scale * float(np.dot(q[i], k[j])) for j in keys]
+        top = max(scores)
+        weights = [math.exp(x - top) for x in scores]
+        total = math.fsum(weights)
+        row = sum(wt * v[j] for wt, j in zip(weights, keys)) / total
+        assert np.allclose(o[0, 0, i], row, rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, i] - (top + math.log(total))) <= 1e-13
 
 
 @pytest.mark.parametrize("causal", [False, True])
