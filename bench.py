@@ -26,6 +26,12 @@ causal), the same count for every backend. Also reported:
   forward with grouped key/value heads, a sliding window and packed sequences, in TFLOP/s
   of the (query, key) pairs each query sees (4 d FLOPs per pair).
 
+``cpu_baseline.per_workload`` times the same oracle on whole heads of every forward workload
+(the FP8 one twice: on the original and on the dequantised inputs).
+
+``--summarize DIR [--kernel RE] [--last K]`` prints kernel-trace and counter statistics of a
+rocprofv3 csv output directory (only each kernel's last K dispatches with --last: the timed
+launches); ``--source-hashes`` prints the code-only hashes of each kernel family's sources.
 ``--calib-copy`` runs only a 1 GiB device-to-device copy (used to calibrate the
 rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
 ``--only-bwd`` times only the backward on the headline shape (for kernel traces
@@ -69,11 +75,24 @@ def parse_args():
     p.add_argument("--only-decode", action="store_true")
     p.add_argument("--only", default=None, help="fp8, or a forward workload name")
     p.add_argument("--only-ext", default=None, help="one grouped-head / window / packed workload")
+    p.add_argument("--source-hashes", action="store_true", help="print the kernel families' source hashes")
+    p.add_argument("--summarize", default=None, metavar="DIR",
+                   help="statistics of a rocprofv3 output directory (kernel trace and/or counters)")
+    p.add_argument("--kernel", default="fwd_kernel", help="--summarize: regular expression of kernel names")
+    p.add_argument("--last", type=int, default=0, help="--summarize: only the last N dispatches of each kernel")
     return p.parse_args()
 
 
-# the sources the headline kernel (bf16 forward) is compiled from
-HEADLINE_SOURCES = ("fa_common.h", "fa_fwd_kernel.h", "fa_fwd_bf16.hip")
+# the sources each kernel family is compiled from (headline: the bf16 forward)
+KERNEL_SOURCES = {
+    "fwd_bf16": ("fa_common.h", "fa_fwd_kernel.h", "fa_fwd_bf16.hip"),
+    "fwd_fp8": ("fa_common.h", "fa_fwd_kernel.h", "fa_fp8.hip"),
+    "fwd_short": ("fa_common.h", "fa_fwd_kernel.h", "fa_tile.h", "fa_fwd_short.hip"),
+    "fwd_f32": ("fa_common.h", "fa_fwd_f32.hip"),
+    "bwd": ("fa_common.h", "fa_fwd_kernel.h", "fa_tile.h", "fa_bwd.hip"),
+    "decode": ("fa_common.h", "fa_fwd_kernel.h", "fa_tile.h", "fa_decode.hip"),
+}
+HEADLINE_SOURCES = KERNEL_SOURCES["fwd_bf16"]
 
 
 def code_only(text: str) -> str:
@@ -85,15 +104,19 @@ def code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the headline kernel's sources (code only), to tell whether stored counter
-    readings of that kernel are still current."""
+def kernel_source_hash(family: str = "fwd_bf16") -> str:
+    """Hash of a kernel family's sources (code only), to tell whether stored measurements of
+    those kernels are still current (the headline's: family fwd_bf16)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_06_amd", "csrc")
-    for name in HEADLINE_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         h.update(name.encode())
         h.update(code_only(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()[:16]
+
+
+def source_hashes() -> dict:
+    return {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES}
 
 
 def read_traffic():
@@ -220,8 +243,134 @@ def cpu_baseline(w, budget_s: float = 15.0):
     }
 
 
+def _short_name(name: str) -> str:
+    """A kernel name without its argument list (the first '(' outside template brackets)."""
+    anon = "(anonymous namespace)"
+    text = name.replace(anon, "\x00")
+    depth = 0
+    for i, ch in enumerate(text):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            text = text[:i]
+            break
+    return text.replace("\x00", anon).strip()
+
+
+def summarize(d: str, kernel_re: str, last: int) -> int:
+    """Statistics of one rocprofv3 ``--output-format csv`` directory for the kernels whose name
+    matches kernel_re: from a kernel trace, per kernel the dispatch count and the average, median,
+    min and max duration; from a counter collection, per kernel and counter the median value per
+    dispatch. With ``last`` > 0 only each kernel's last `last` dispatches count (in dispatch
+    order): the timed launches of a bench run, after its warm-up."""
+    import csv
+    import glob
+    import statistics
+    from collections import defaultdict
+
+    rx = re.compile(kernel_re)
+    found = False
+    for f in sorted(glob.glob(os.path.join(d, "*kernel_trace.csv"))):
+        found = True
+        by = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if rx.search(r["Kernel_Name"]):
+                by[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        print(f"# kernel trace {os.path.basename(f)}: kernels matching '{kernel_re}'"
+              + (f", last {last} dispatches of each" if last else ", every dispatch"))
+        print("# columns: kernel | dispatches | used | average ns | median ns | min ns | max ns")
+        for name, ts in sorted(by.items()):
+            ts.sort()
+            sel = ts[-last:] if last else ts
+            du = [e - b for b, e in sel]
+            print(f"{_short_name(name)} | {len(ts)} | {len(sel)} | {statistics.mean(du):.0f} | "
+                  f"{statistics.median(du):.0f} | {min(du)} | {max(du)}")
+    for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
+        found = True
+        vals = defaultdict(lambda: defaultdict(float))   # (kernel, dispatch) -> counter -> value
+        for r in csv.DictReader(open(f)):
+            if rx.search(r["Kernel_Name"]):
+                vals[(r["Kernel_Name"], int(r["Dispatch_Id"]))][r["Counter_Name"]] += float(r["Counter_Value"])
+        per_kernel = defaultdict(list)
+        for (name, disp), cv in vals.items():
+            per_kernel[name].append((disp, cv))
+        print(f"# counters {os.path.basename(f)}: median per dispatch, kernels matching '{kernel_re}'"
+              + (f", last {last} dispatches of each" if last else ", every dispatch"))
+        for name, rows in sorted(per_kernel.items()):
+            rows.sort()
+            sel = rows[-last:] if last else rows
+            print(f"## {_short_name(name)} ({len(sel)} of {len(rows)} dispatches)")
+            for c in sorted(sel[0][1]):
+                print(f"{c}: {statistics.median(cv[c] for _, cv in sel):.6g}")
+    if not found:
+        print(f"no kernel trace or counter collection in {d}", file=sys.stderr)
+        return 1
+    return 0
+
+
+def cpu_oracle_per_workload(budget_s: float = 2.0) -> dict:
+    """The float64 oracle on whole heads of every forward workload, each until ~budget_s of CPU
+    work (at least one head; every head of the small ones), on the same seeded inputs as the GPU
+    runs. The oracle materialises the full score matrix, causal or not: fp64 FLOPs done are
+    4 N^2 d per head; "attention_TFLOP/s" counts them as the GPU figures do (halved for causal).
+    The FP8 workload twice: on the original float32 inputs (the O_true reference) and on the
+    dequantised rotated inputs (O_deq; the quantisation itself untimed)."""
+    import numpy as np
+
+    from exact_attention_06_amd.workloads import WORKLOADS, make_fp8_inputs, make_qkv
+    from oracle.attention import attention_head_fp64
+    from oracle.fp8 import block_dequantize, block_quantize, rotate_to_f32
+
+    def run(w, causal, heads_fn):
+        heads, secs = 0, 0.0
+        while heads < w.B * w.H and (heads == 0 or secs < budget_s):
+            b, h = divmod(heads, w.H)
+            args = heads_fn(b, h)
+            t0 = time.perf_counter()
+            attention_head_fp64(*args, w.scale, causal)
+            secs += time.perf_counter() - t0
+            heads += 1
+        done = heads * 4.0 * w.N * w.N * w.d
+        counted = done / (2 if causal else 1)
+        return {"heads_timed": heads, "heads": w.B * w.H, "seconds": round(secs, 3),
+                "fp64_GFLOP/s": round(done / secs / 1e9, 1), "attention_TFLOP/s": round(counted / secs / 1e12, 4),
+                "whole_workload_s_est": round(secs / heads * w.B * w.H, 1)}
+
+    out = {}
+    for name, causal in [("tiny_f32", False), ("b4h16n2k_d128", False), ("b4h16n2k_d128", True),
+                         ("long_n16k_d128", True), ("b8h16n4k_d64", False), ("b8h16n4k_d256", False),
+                         ("b4h16n8k_d128", False), ("b4h16n8k_d128", True)]:
+        w = WORKLOADS[name]
+        q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype)
+        out[f"{name}{'_causal' if causal else ''}"] = run(w, causal, lambda b, h: (q[b, h], k[b, h], v[b, h]))
+        del q, k, v
+        progress(f"cpu oracle {name} causal={causal} done")
+    w = WORKLOADS["fp8_b4h16n8k_d128"]
+    q, k, v, signs = make_fp8_inputs(w.B, w.H, w.N, w.d, w.seed)
+    sg = signs.numpy()
+    out["fp8_b4h16n8k_d128_O_true"] = run(w, False, lambda b, h: (q[b, h], k[b, h], v[b, h]))
+
+    def deq(b, h):
+        qc, qs = block_quantize(rotate_to_f32(q[b, h].numpy(), sg))
+        kc, ks = block_quantize(rotate_to_f32(k[b, h].numpy(), sg))
+        vc, vs = block_quantize(v[b, h].numpy())
+        return (block_dequantize(qc, qs), block_dequantize(kc, ks), block_dequantize(vc, vs))
+    out["fp8_b4h16n8k_d128_O_deq"] = run(w, False, deq)
+    progress("cpu oracle fp8 done")
+    del q, k, v
+    _ = np
+    return out
+
+
 def main():
     args = parse_args()
+    if args.summarize is not None:
+        return summarize(args.summarize, args.kernel, args.last)
+    if args.source_hashes:
+        print(json.dumps(source_hashes()))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs "
               "on one GPU per call and the attention forward is not sharded across GPUs.", file=sys.stderr)
@@ -313,7 +462,7 @@ def main():
         k8, sk = fa_prep_fp8(k, signs)
         v8, sv = fa_prep_fp8(v)
         del q, k, v
-        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.float32, device="cuda")
         lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device="cuda")
         m = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), args.steps, args.warmup, 100.0)
         print(json.dumps({"metric": "attention fwd TFLOP/s (4*B*H*N^2*d), e4m3 inputs", "value": round(wf.flops(False) / m / 1e9, 1),
@@ -403,7 +552,7 @@ def main():
         q8, sq = fa_prep_fp8(q, signs)
         k8, sk = fa_prep_fp8(k, signs)
         v8, sv = fa_prep_fp8(v)
-        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((wf.B, wf.H, wf.N, wf.d), dtype=torch.float32, device="cuda")
         lse = torch.empty((wf.B, wf.H, wf.N), dtype=torch.float32, device="cuda")
         m_fwd = time_launches(torch, lambda: fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse), s2, w2, 100.0)
         m_prep = time_launches(torch, lambda: fa_prep_fp8(q, signs, q8, sq), s2, w2, 100.0)
@@ -466,9 +615,12 @@ def main():
                                   "attention_frac_of_gemm": round(tflops / gemm_tflops, 4)}
     del a, b, c
     progress(f"calibration gemm {gemm_tflops:.1f} TFLOP/s")
+    result["source_hashes"] = source_hashes()
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)
         progress("cpu baseline done")
+        if not args.only_headline:
+            result["cpu_baseline"]["per_workload"] = cpu_oracle_per_workload()
     print(json.dumps(result))
     return 0
 

@@ -170,7 +170,7 @@ def fa_prep_fp8(x, signs=None, x8=None, s=None, *, stream=None):
 
 
 def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=False, want_lse=True, stream=None):
-    """Attention forward on e4m3 codes with per-64-row scales; returns (o bfloat16, lse)."""
+    """Attention forward on e4m3 codes with per-64-row scales; returns (o float32, lse)."""
     B, H, N, d = _bhnd(q8)
     for t in (q8, k8, v8):
         if t.dtype != torch.uint8 or t.shape != q8.shape:
@@ -180,10 +180,10 @@ def fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o=None, lse=None, *, scale=None, causal=F
         if t.dtype != torch.float32 or tuple(t.shape) != (B, H, nsb):
             raise ValueError("scales must be float32 [B, H, ceil(N/64)]")
     if o is None:
-        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    _expect(o, (B, H, N, d), torch.bfloat16, "o")
+    _expect(o, (B, H, N, d), torch.float32, "o")
     _expect(lse, (B, H, N), torch.float32, "lse")
     _require_gpu(q8, k8, v8, sq, sk, sv, o, lse)
     scale = (1.0 / d ** 0.5) if scale is None else float(scale)

@@ -14,11 +14,14 @@
 // instruction of a quad reads 64 contiguous bytes. The fast Walsh-Hadamard transform pairs
 // elements along one index bit per butterfly stage, in any order: the bits of j and k are
 // stages inside the thread, the two bits of q are stages across the quad (DPP quad
-// permutations, no LDS). Then one multiply by +-1/sqrt(d)
-// applies the signs and the normalisation, the block amax is reduced, s = amax / 448, and
+// permutations, no LDS), all in fp64; then one multiply by +-1/sqrt(d) applies the signs and
+// the normalisation and the result is rounded once to fp32 (the definition's x M to within
+// ~1e-16 relative; an fp32 transform rounds at every stage and moves a few values per
+// million to the neighbouring E4M3 code). The block amax is reduced, s = amax / 448, and
 // the codes are e4m3(x / s) with the hardware RNE convert. x / s is the correctly rounded
 // fp32 quotient, computed from r = RN(1/s) as q0 = x r, q = q0 + (x - q0 s) r (two FMAs;
-// Markstein's correction gives RN(x / s) for normal operands) instead of a full division.
+// Markstein's correction gives RN(x / s) for normal operands; the sign is copied from x so that
+// -0 stays -0) instead of a full division.
 // No clamp is needed for a normal s: |x| <= amax gives |x / s| <= 448 (1 + 2^-23), which the
 // convert rounds to 448; only a subnormal s (amax below ~5e-36) can exceed that, and such
 // blocks take a clamping branch. NaN inputs stay NaN.
@@ -27,6 +30,8 @@
 // The FP8 forward itself is the shared fused kernel (fa_fwd_kernel.h) instantiated for e4m3
 // Q, K, V: e4m3 QK^T on the matrix cores with the block scales folded into the softmax FMA,
 // V expanded exactly to bf16 in LDS with its block scale carried by P, bf16 P.
+#include <cmath>
+
 #include "fa_common.h"
 #include "fa_fwd_kernel.h"
 #include "fa_internal.h"
@@ -49,11 +54,18 @@ __device__ __forceinline__ float quad_xor1(float x) {
 __device__ __forceinline__ float quad_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
 }
+// the same for an fp64 value (its two 32-bit halves)
+template <int CTRL>
+__device__ __forceinline__ double quad_xor_d(double x) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xF, 0xF, true);
+    return __hiloint2double(hi, lo);
+}
 
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
                                                             float* __restrict__ S, const float* __restrict__ signs,
-                                                            int N, int nsb, float inv_sqrt_d) {
+                                                            int N, int nsb, double inv_sqrt_d) {
     constexpr int NV = D / 4;   // values per thread: x[4 k + j] is element 16 k + 4 qd + j
     __shared__ float wmax[kPrepThreads / kWave];
     const int tid = threadIdx.x;
@@ -76,31 +88,37 @@ __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __r
         x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
     }
     if (signs != nullptr) {
+        // the rotation in fp64, rounded once to fp32: the partial sums of the transform are exact
+        // in fp64 for fp32 inputs of moderate range, so the result is x M to within ~1e-16
+        // relative, the float64 product of the definition, and rounds to the same fp32 value
+        // except within ~1e-15 of a rounding midpoint
+        double y[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) y[i] = (double)x[i];
         // in-thread butterflies: register strides 1 .. NV/2 (element bits 0, 1 and 4 ..)
 #pragma unroll
         for (int st = 1; st < NV; st <<= 1)
 #pragma unroll
             for (int i = 0; i < NV; ++i)
                 if ((i & st) == 0) {
-                    const float a = x[i], b = x[i + st];
-                    x[i] = a + b;
-                    x[i + st] = a - b;
+                    const double a = y[i], b = y[i + st];
+                    y[i] = a + b;
+                    y[i + st] = a - b;
                 }
         // cross-thread butterflies: element bits 2 and 3 (lane xor 1, xor 2); the lower
         // partner keeps x + y, the upper one y - x, i.e. (+-x) + y
-        const float sg1 = (qd & 1) ? -1.f : 1.f;
-        const float sg2 = (qd & 2) ? -1.f : 1.f;
-        // (x * +-1 is exact; a separate add, not an FMA, takes the DPP operand)
+        const double sg1 = (qd & 1) ? -1.0 : 1.0;
+        const double sg2 = (qd & 2) ? -1.0 : 1.0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) x[i] = __fadd_rn(quad_xor1(x[i]), __fmul_rn(x[i], sg1));
+        for (int i = 0; i < NV; ++i) y[i] = __dadd_rn(quad_xor_d<0xB1>(y[i]), __dmul_rn(y[i], sg1));
 #pragma unroll
-        for (int i = 0; i < NV; ++i) x[i] = __fadd_rn(quad_xor2(x[i]), __fmul_rn(x[i], sg2));
-        // signs and 1/sqrt(d) in one multiply: x (+-c) = +-(x c), the same bits as (x c) (+-1)
+        for (int i = 0; i < NV; ++i) y[i] = __dadd_rn(quad_xor_d<0x4E>(y[i]), __dmul_rn(y[i], sg2));
+        // signs and 1/sqrt(d) in one multiply (+-c is exact), then the one rounding to fp32
 #pragma unroll
         for (int i = 0; i < NV; i += 4) {
             const f32x4 sv = *(const f32x4*)(signs + 4 * i + 4 * qd);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) x[i + u] *= sv[u] * inv_sqrt_d;
+            for (int u = 0; u < 4; ++u) x[i + u] = (float)(y[i + u] * ((double)sv[u] * inv_sqrt_d));
         }
     }
     // block amax
@@ -120,7 +138,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __r
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const float q0 = __fmul_rn(x[i], r);
-        x[i] = __builtin_fmaf(__builtin_fmaf(-q0, s, x[i]), r, q0);   // RN(x / s)
+        // RN(x / s); the correction turns a -0 quotient into +0, so the sign is taken from x
+        // (s > 0: x / s has the sign of x, and E4M3 keeps -0 as its own code)
+        x[i] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x[i]), r, q0), x[i]);
     }
     if (tiny) {   // uniform per block, rare
 #pragma unroll
@@ -143,7 +163,7 @@ hipError_t launch_prep(const float* x, void* x8, float* s, const float* signs, i
     const long long total = (long long)BH * nsb;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((prep_fp8_kernel<D>), dim3((unsigned)total), dim3(kPrepThreads), 0, stream, x, (uint8_t*)x8, s,
-                       signs, N, nsb, 1.0f / sqrtf((float)D));
+                       signs, N, nsb, 1.0 / std::sqrt((double)D));
     return hipGetLastError();
 }
 

@@ -40,12 +40,14 @@
 // - Q8 and K8 are e4m3 with one fp32 scale per 64 rows; a key block (32 or 64 keys) and a
 //   32-query tile each lie inside one scale block, so the score of the block is
 //   s_Q s_K (Q8 K8^T) and s_Q s_K is folded into the FMA that subtracts the running max;
-// - V stays e4m3 in HBM and is expanded exactly to bf16 when it is written to LDS (every
-//   e4m3 value is a bf16 value); its block scale rides on P: P_j is computed as
+// - V stays e4m3 in HBM and is expanded exactly to fp16 when it is written to LDS (every
+//   e4m3 value is an fp16 value); its block scale rides on P: P_j is computed as
 //   exp2(S ct - m + log2(s_V(j) / max s_V)) in the same FMA (no extra per-element work),
 //   the row sum divides the ratio back out once per block, and max s_V is applied with the
-//   final division. P is rounded to bf16, not e4m3, for the PV product: with e4m3 P the
-//   output error on inputs with outliers is an order of magnitude above the 6e-2 budget.
+//   final division. P is rounded to fp16 (11 significant bits), not e4m3, for the PV product
+//   (v_mfma_f32_32x32x16_f16, the bf16 rate): the outliers put values of magnitude up to ~70
+//   into V, and with e4m3 P (or bf16 P) one dominant probability's rounding alone moves such
+//   an output by more than the 6e-2 budget. For the same reason O is written in fp32.
 #pragma once
 
 #include <type_traits>
@@ -219,12 +221,15 @@ template <InKind KIND, int D, int BC, int NQ, bool CAUSAL, int TAU, int MINB, bo
 __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    bf16_t* __restrict__ O, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */,
+    void* __restrict__ Ov, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */,
     FwdExt ext) {
     static_assert(!(EXT && KIND == InKind::FP8), "extended problems take bf16 inputs");
     constexpr int NT = 64 * WAVES;    // threads per workgroup
     using C = FwdCfg<KIND, D, BC, NT>;
     using QT = typename QOperand<KIND>::type;
+    // operands of the PV product: bf16 P and V, or (FP8 inputs) fp16 P and V
+    using PT = typename std::conditional<C::F8, f16x8, bf16x8>::type;
+    using PE = typename std::conditional<C::F8, _Float16, bf16_t>::type;
     constexpr float tau = (float)TAU;
     static_assert(DSPLIT == 1 || (DSPLIT == 2 && !C::F8 && PIPE && WAVES % 2 == 0), "d split: bf16, pipelined, wave pairs");
     constexpr int BR = WAVES / DSPLIT * 32 * NQ;   // queries per workgroup
@@ -400,19 +405,19 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 lds_dma16(rV, dst + 1024 * (wave + WAVES * i), voff_of(i) + kb * C::ROW_BYTES);
         }
     };
-    // FP8: expand the staged e4m3 V chunks exactly to bf16 and store them swizzled
+    // FP8: expand the staged e4m3 V chunks exactly to fp16 and store them swizzled
     auto store_v = [&](uint8_t* dst) {
         if constexpr (C::F8) {
 #pragma unroll
             for (int i = 0; i < C::V_LOADS; ++i) {
                 const int x = tid + NT * i;
                 const int r = x / (D / 16);
-                const int c8 = x % (D / 16);   // 16 e4m3 values = bf16 chunks 2 c8 and 2 c8 + 1
+                const int c8 = x % (D / 16);   // 16 e4m3 values = fp16 chunks 2 c8 and 2 c8 + 1
                 i32x4 lo, hi;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int wa = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[i][u], 1.f, false));
-                    const int wb = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vst[i][u], 1.f, true));
+                    const int wa = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, false));
+                    const int wb = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, true));
                     if (u < 2) { lo[2 * u] = wa; lo[2 * u + 1] = wb; }
                     else { hi[2 * (u - 2)] = wa; hi[2 * (u - 2) + 1] = wb; }
                 }
@@ -649,12 +654,12 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             inv_r = svmax * __builtin_amdgcn_rcpf(sv);
         }
         const float ks = kscale(j);
-        // the wave's last block under a causal mask or a window's right edge holds its diagonal:
-        // the first rows of a head see only a few keys there, and rounding P to bf16 would cost
-        // up to 2^-9 of the largest value's magnitude. There P is carried as P_hi + P_lo (two
-        // bf16 terms, 2^-17 relative) and the block takes two PV products.
-        constexpr bool SPLITP = PER_WAVE && !NEXT;
-        bf16x8 pf[NQ][C::CH];
+        // causal: the wave's last block holds its diagonal. The first rows of a head see only a
+        // few keys there, and rounding P to bf16 would cost up to 2^-9 of the largest value's
+        // magnitude; there P is carried as P_hi + P_lo (two bf16 terms, 2^-17 relative) and the
+        // block takes two PV products.
+        constexpr bool SPLITP = CAUSAL && !NEXT && !C::F8;
+        PT pf[NQ][C::CH];
         bf16x8 plo[SPLITP ? NQ : 1][SPLITP ? C::CH : 1];
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
@@ -670,7 +675,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                     // fp32 P: the logsumexp needs the unrounded sum (started at the first term,
                     // not at 0, which would cost an add)
                     lsum = (t == 0 && i == 0) ? p : lsum + p;
-                    const bf16_t ph = (bf16_t)p;
+                    const PE ph = (PE)p;
                     pf[n][2 * t + i / 8][i % 8] = ph;
                     if constexpr (SPLITP) plo[n][2 * t + i / 8][i % 8] = (bf16_t)(p - (float)ph);   // p - ph is exact
                 }
@@ -689,13 +694,19 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                 const uint8_t* vp = vt + 16 * ch * C::VROW_BYTES + vhd + 256 * (e / 4) + vaddr[e % 4];
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp));
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(FA_LDS(bf16x4, vp + 4 * C::VROW_BYTES));
-                // concatenated as whole vectors (element-wise assembly is mis-compiled)
+                // concatenated as whole vectors (element-wise assembly is mis-compiled); the
+                // transposing read moves 16-bit elements, so FP8's fp16 V is read the same way
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n) {
-                    acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[n][ch], acc[n][e], 0, 0, 0);
-                    if constexpr (SPLITP)
-                        acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, plo[n][ch], acc[n][e], 0, 0, 0);
+                    if constexpr (C::F8) {
+                        acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), pf[n][ch],
+                                                                          acc[n][e], 0, 0, 0);
+                    } else {
+                        acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[n][ch], acc[n][e], 0, 0, 0);
+                        if constexpr (SPLITP)
+                            acc[n][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, plo[n][ch], acc[n][e], 0, 0, 0);
+                    }
                 }
             }
         // ---- mask and row max of block j+1 (d split: at the start of step j+1, after the exchange)
@@ -781,10 +792,35 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         }
     }
 
-    // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2. Each wave stages its 32 x d bf16
-    // tile of O in LDS (the tile slots are free after the last barrier) and writes it back in
-    // whole rows, 16 bytes per lane: a lane's own results are 4-element runs scattered over
-    // the d range, which would make every store instruction touch 32 rows.
+    // ---- epilogue: O = O~ / l, LSE = (m + log2 l) ln 2.
+    if constexpr (C::F8) {
+        // fp32 O, straight from the accumulators: register 4a + b of d tile e holds
+        // d = 32 e + 8 a + 4 h + b of query col, so each lane writes whole 16-byte runs
+        float* const O = (float*)Ov;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
+            const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
+            if (qrow[n] < N) {
+                float* const orow = O + head_off + (size_t)qrow[n] * D + 4 * h;
+#pragma unroll
+                for (int e = 0; e < DTW; ++e)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        *(f32x4*)(orow + 32 * e + 8 * a) =
+                            f32x4{acc[n][e][4 * a] * inv, acc[n][e][4 * a + 1] * inv, acc[n][e][4 * a + 2] * inv,
+                                  acc[n][e][4 * a + 3] * inv};
+                if (LSE != nullptr && h == 0)
+                    LSE[qbase + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
+            }
+        }
+        return;
+    }
+    // bf16 O: each wave stages its 32 x d tile in LDS (the tile slots are free after the last
+    // barrier) and writes it back in whole rows, 16 bytes per lane: a lane's own results are
+    // 4-element runs scattered over the d range, which would make every store instruction touch
+    // 32 rows.
+    bf16_t* const O = (bf16_t*)Ov;
     constexpr int DW = D / DSPLIT;                     // columns of O this wave writes
     constexpr int OROW = DW * 2;                       // bytes per staged bf16 row
     constexpr int OSTAGE = 32 * OROW;                  // one wave's tile
@@ -855,7 +891,7 @@ hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const 
         total = std::min(total, (long long)ext.Hq * (((long long)ext.ntot + (long long)ext.nseq * (BR - 1)) / BR));
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT, DSPLIT>), dim3((unsigned)total),
-                       dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, (bf16_t*)o, lse, N, numQB, nsb, scale * kLog2e, ext);
+                       dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, o, lse, N, numQB, nsb, scale * kLog2e, ext);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ hipError_t launch_fwd_f32(const void* q, const void* k, const void* v, void* o, 
 hipError_t launch_prep_fp8(const float* x, void* x8, float* s, const float* signs, int BH, int N, int d,
                            hipStream_t stream);
 
-// e4m3 q8, k8, v8 [BH, N, d] with scales [BH, ceil(N/64)] -> bf16 O [BH, N, d], lse [BH, N] or null.
+// e4m3 q8, k8, v8 [BH, N, d] with scales [BH, ceil(N/64)] -> fp32 O [BH, N, d], lse [BH, N] or null.
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                           const float* sv, void* o, float* lse, int BH, int N, int d, float scale, bool causal,
                           hipStream_t stream);

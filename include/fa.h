@@ -111,13 +111,14 @@ int fa_prep_fp8(const float* x, void* x8, float* s, const float* signs,
  * softmax statistics and the output accumulator stay in high precision
  * ("FlashAttention 2 & 3" page, section "What stays in higher precision").
  * The pages also convert P to FP8 for the second product; this library keeps
- * P (and V, expanded exactly from E4M3) in bfloat16 for it, since an E4M3 P
- * costs an order of magnitude more output error on inputs with outliers.
+ * P (and V, expanded exactly from E4M3) in fp16 for it and writes O in fp32:
+ * inputs with outliers put values of magnitude up to ~70 into O, where an E4M3
+ * or bf16 P, or a bf16 O, alone costs more than 6e-2 of output error.
  *
  *   q8, k8, v8  [B, H, N, d] E4M3 codes (as written by fa_prep_fp8; Q and K
  *               rotated with the same signs, V usually not rotated).
  *   sq, sk, sv  [B, H, ceil(N/64)] fp32 block scales of q8, k8, v8.
- *   o           [B, H, N, d] bfloat16 (output) = the attention of the
+ *   o           [B, H, N, d] fp32 (output) = the attention of the
  *               dequantised inputs (if V was rotated, O is in the rotated basis).
  *   lse         [B, H, N] fp32 (output) or NULL, as in fa_fwd.
  *   d           64, 128 or 256.  scale, causal: as in fa_fwd.

@@ -3,8 +3,11 @@
 Bounds for every parity case whose inputs are iid N(0, 1) (the five workloads, the headline
 and the smaller shapes and edge cases built the same way):
 - bf16 output O: max |O_gpu - O_ref| <= 1e-2 over every element, and mean <= 1e-3;
-- LSE: relative error |LSE_gpu - LSE_ref| / |LSE_ref| <= 1e-4 for every row (the
-  "max(1, |LSE_ref|)" form, an absolute floor of 1e-4 near LSE = 0, is printed beside it);
+- LSE: |LSE_gpu - LSE_ref| <= 1e-4 max(1, |LSE_ref|) for every row: the relative error, with
+  an absolute floor of 1e-4 for rows whose LSE is near 0. Such rows exist in the causal and
+  packed workloads (|LSE_ref| down to ~1e-3, where m and log l nearly cancel): there the fp32
+  rounding of the two terms alone, ~2e-7 absolute, is a relative error of ~2e-4, which no fp32
+  computation avoids. The pure relative error is printed beside it;
 - fp32 output (fp32 arithmetic throughout): max abs <= 2e-5, LSE relative 1e-5. fp32
   rounding (2^-24 per operation) over sums of a few hundred terms of magnitude <= 1 and the
   ~1-ulp hardware exp2 stay two orders of magnitude below this;
@@ -129,7 +132,7 @@ class Tally:
         assert self.count > 0
         assert self.max <= max_abs, f"{self.label}: max|dO| {self.max:.4g} > {max_abs}"
         assert self.mean <= mean_abs, f"{self.label}: mean|dO| {self.mean:.4g} > {mean_abs}"
-        assert self.lse_rel <= lse_rel, f"{self.label}: LSE relative error {self.lse_rel:.3g} > {lse_rel}"
+        assert self.lse_floor <= lse_rel, f"{self.label}: LSE error {self.lse_floor:.3g} > {lse_rel} max(1, |LSE|)"
 
 
 def all_finite(*ts):

@@ -132,7 +132,7 @@ def test_python_binding_checks_given_outputs(L):
     c8 = torch.zeros(1, 2, 64, 64, dtype=torch.uint8)
     sc = torch.ones(1, 2, 1)
     with pytest.raises(ValueError, match="o must be"):
-        fa_fwd_fp8(c8, c8, c8, sc, sc, sc, o=torch.empty(1, 2, 64, 64))   # the fp8 forward writes bfloat16
+        fa_fwd_fp8(c8, c8, c8, sc, sc, sc, o=torch.empty(1, 2, 64, 64, dtype=torch.bfloat16))   # it writes float32
 
 
 def test_python_binding_rejects_mixed_devices():

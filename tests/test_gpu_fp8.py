@@ -5,10 +5,11 @@
 - With rotation, on inputs whose fast Walsh-Hadamard transform is exact in float32 (small
   integers times a power of two, with outliers) at d = 64 and d = 256, where 1/sqrt(d) is a
   power of two: the rotated values are then exact on both sides, and the GPU's codes and
-  scales equal the oracle's bit for bit. On general inputs the GPU's float32 transform differs
-  from the oracle's float64 product by a few float32 ulps, so a code may differ where the
-  rotated value lies next to a rounding midpoint: codes agree except for a tiny fraction, and
-  those are neighbouring E4M3 values; scales agree to 1e-6.
+  scales equal the oracle's bit for bit. On general inputs both sides rotate in float64 (the
+  GPU by a fast transform, the oracle by a dense product) and round once to float32; they
+  agree to ~1e-16 relative, so the float32 values, and hence the scales and codes, are the
+  same unless a value lies within ~1e-15 of a rounding midpoint: bit for bit on the small
+  shapes, and at most a few codes (neighbouring E4M3 values) in the 201M of the workload.
 - fa_fwd_fp8 is compared with attention on the dequantised inputs (O_deq, LSE_deq) over the
   whole output: max |dO| <= 6e-2, mean <= 1e-3, LSE relative <= 1e-4. The FP8 workload is
   checked twice at full size: on the oracle's codes, and through the GPU's own rotation and
@@ -43,7 +44,7 @@ def prep(x, signs=None):
 
 def fwd(q8, k8, v8, sq, sk, sv, causal=False):
     B, H, N, d = q8.shape
-    o = nan_out((B, H, N, d), torch.bfloat16)
+    o = nan_out((B, H, N, d), torch.float32)
     lse = nan_out((B, H, N), torch.float32)
     fa_fwd_fp8(q8, k8, v8, sq, sk, sv, o, lse, causal=causal)
     torch.cuda.synchronize()
@@ -81,14 +82,8 @@ def test_prep_with_rotation(shape):
     x, _, _, signs = make_fp8_inputs(*shape, seed=22)
     x8, s = prep(x, signs)
     codes, scales = block_quantize(rotate_to_f32(x.numpy(), signs.numpy()))
-    np.testing.assert_allclose(s.cpu().numpy(), scales, rtol=1e-6)
-    g = x8.cpu().numpy()
-    diff = g != codes
-    assert diff.mean() <= 1e-3
-    # where codes differ they must be neighbouring values (one E4M3 step apart)
-    dg, dr = e4m3_decode(g[diff]), e4m3_decode(codes[diff])
-    step = np.maximum(np.abs(dr), 2.0 ** -6) * 2.0 ** -3
-    assert (np.abs(dg - dr) <= step * 1.0001).all()
+    assert np.array_equal(s.cpu().numpy(), scales)
+    assert np.array_equal(x8.cpu().numpy(), codes)
 
 
 def check_vs_deq(o, lse, o_deq, lse_deq, label, o_true=None):
@@ -102,7 +97,8 @@ def check_vs_deq(o, lse, o_deq, lse_deq, label, o_true=None):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(1, 2, 300, 128), (2, 2, 128, 64), (1, 1, 200, 256), (1, 1, 1, 128)])
+@pytest.mark.parametrize("shape", [(1, 2, 300, 128), (2, 2, 128, 64), (1, 1, 200, 256), (1, 1, 1, 128),
+                                   (1, 2, 2100, 128)])
 def test_fwd_fp8_small(shape, causal):
     say(f"fwd fp8 {shape} causal={causal}")
     B, H, N, d = shape
@@ -140,8 +136,16 @@ def test_fp8_workload_whole_output():
     k8, sk = prep(k, signs)
     v8, sv = prep(v)
     o2, l2 = fwd(q8, k8, v8, sq, sk, sv)
-    ncode = sum(int((a.cpu().numpy() != qi[n]).sum()) for a, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")))
+    ncode = 0
+    for a, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        g = a.cpu().numpy()
+        diff = g != qi[n]
+        ncode += int(diff.sum())
+        # where codes differ (a rotated value within ~1e-15 of a midpoint) they are neighbours
+        dg, dr = e4m3_decode(g[diff]), e4m3_decode(qi[n][diff])
+        assert (np.abs(dg - dr) <= np.maximum(np.abs(dr), 2.0 ** -6) * 2.0 ** -3 * 1.0001).all()
     say(f"  GPU codes differing from the oracle's: {ncode} of {3 * q.numel()}")
+    assert ncode <= 64
     del q8, k8, v8
     o1c, l1c, o2c, l2c = o1.float().cpu(), l1.cpu(), o2.float().cpu(), l2.cpu()
     t1, t2 = Tally(f"{w.name} on the oracle's codes"), Tally(f"{w.name} GPU prep -> GPU forward")
