@@ -12,13 +12,14 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 - ``fa_fwd_ext(q, k, v, window=..., cu_seqlens=...)``: the forward with grouped
   key/value heads, a sliding window and packed variable-length sequences;
 - ``fa_decode(q, k, v, ...)``: a few query positions against a long key/value
-  cache (grouped heads allowed), split over the keys and merged.
+  cache (grouped heads allowed), split over the keys and merged;
+  ``fa_decode_noalloc`` does the same with the library's static scratch.
 
 ``workloads`` draws the seeded synthetic inputs; ``build`` compiles the library.
 """
 
-from ._lib import (FAError, fa_bwd, fa_decode, fa_decode_workspace_size, fa_fwd,  # noqa: F401
+from ._lib import (FAError, fa_bwd, fa_decode, fa_decode_noalloc, fa_decode_workspace_size, fa_fwd,  # noqa: F401
                    fa_fwd_ext, fa_fwd_fp8, fa_prep_fp8, lib, status_string)
 
-__all__ = ["FAError", "fa_bwd", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ext",
+__all__ = ["FAError", "fa_bwd", "fa_decode", "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_ext",
            "fa_fwd_fp8", "fa_prep_fp8", "lib", "status_string"]

@@ -21,10 +21,10 @@ FA_F32 = 0
 FA_BF16 = 1
 STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_ALIGN", -3: "FA_ERR_SHAPE", -4: "FA_ERR_HEADDIM",
-    -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
+    -5: "FA_ERR_DTYPE", -6: "FA_ERR_SCALE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG", -9: "FA_ERR_SCRATCH",
 }
 EXPORTED = ("fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_ext", "fa_decode_workspace_size", "fa_decode",
-            "fa_status_string", "fa_version")
+            "fa_decode_noalloc", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_size.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = i
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_decode_noalloc.restype = i
     L.fa_status_string.argtypes = [i]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_version.argtypes = []
@@ -286,4 +288,25 @@ def fa_fwd_ext(q, k, v, o=None, lse=None, *, scale=None, causal=False, window=(-
     _check(lib().fa_fwd_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, scale,
                             int(bool(causal)), int(window[0]), int(window[1]), _ptr(cu_seqlens), int(max_seqlen),
                             FA_BF16, _stream(stream, q.device)))
+    return o, lse
+
+
+def fa_decode_noalloc(q, k, v, o, lse=None, *, scale=None, causal=False, stream=None):
+    """fa_decode with the library's static scratch instead of a workspace: the C entry point
+    allocates nothing. o (bfloat16 [B, Hq, Nq, d]) must be given; lse (float32 [B, Hq, Nq]) is
+    optional. Calls that overlap in time on one GPU share the scratch and race."""
+    B, Hq, Nq, d = _bhnd(q)
+    Bk, Hkv, Nk, dk = _bhnd(k)
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with the batch and head dim of q")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("fa_decode_noalloc takes bfloat16 tensors")
+    if o is None:
+        raise ValueError("fa_decode_noalloc writes into a given output tensor")
+    _expect(o, (B, Hq, Nq, d), torch.bfloat16, "o")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _require_gpu(q, k, v, o, lse)
+    scale = (1.0 / d ** 0.5) if scale is None else float(scale)
+    _check(lib().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, scale,
+                                   int(bool(causal)), FA_BF16, _stream(stream, q.device)))
     return o, lse

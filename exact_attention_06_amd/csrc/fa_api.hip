@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;   // 0.4.0: fa_fwd_ext
+constexpr int kVersion = 500;   // 0.5.0: fa_decode_noalloc
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -147,6 +147,22 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
                                            static_cast<hipStream_t>(stream)));
 }
 
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
+    int st = check_decode(B, Hq, Hkv, Nq, Nk, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_DTYPE;
+    if ((long long)B * Hq * Nq == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    if (fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).ws_bytes > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (fa::decode_scratch(s, &ws) != hipSuccess) return FA_ERR_LAUNCH;
+    return from_hip(fa::launch_decode_bf16(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, s));
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
@@ -158,6 +174,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_ARG: return "invalid argument (causal not 0/1, or a workspace smaller than required)";
+        case FA_ERR_SCRATCH: return "the problem needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }

@@ -27,16 +27,26 @@
 //
 // Causal reading: the Nq queries are the last Nq positions; row (gi, i) sees keys
 // j <= Nk - Nq + i. Scores are kept in log2 units (S scale log2 e).
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_fwd_kernel.h"   // kBufferConfig
 #include "fa_internal.h"
 #include "fa_tile.h"
+
+// Split states of the allocation-free entry point (fa_decode_noalloc): one copy per GPU, held
+// until the process ends. Host code never passes this name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the per-device address that hipGetSymbolAddress
+// returns (fa::decode_scratch).
+static __device__ __align__(256) uint8_t scratch[fa::kDecodeScratchBytes];
 
 namespace fa {
 namespace {
 
 // workgroups a decoding launch aims for (one resident per compute unit)
 constexpr int kDecTargetWG = 256;
+// the static scratch holds the largest workspace this plan can ask for (see decode_plan)
+static_assert(kDecodeScratchBytes == (size_t)(2 * kDecTargetWG - 2) * 32 * (128 + 2) * 4, "decode scratch bound");
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr float kDecSentinel = -1e30f;   // running max before any visible key (finite: exp2(x - m) stays defined)
@@ -354,6 +364,37 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     if (p.nsplit < 1) p.nsplit = 1;
     p.ws_bytes = p.nsplit > 1 ? (size_t)B * Hkv * p.nsplit * R * (size_t)(d + 2) * 4 : 0;
     return p;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+    int dev = 0;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        // once per device, with that device current: the address of its copy of the array
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, int B,

@@ -55,6 +55,16 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
+// The largest decode_plan(...).ws_bytes of any shape: a plan splits only when its B Hkv ncg
+// groups are fewer than the 256 workgroups it aims for, into at most ceil(256 / groups) splits,
+// so groups x splits <= 510; each holds at most 32 ncg rows of d + 2 fp32 values (d <= 128).
+constexpr size_t kDecodeScratchBytes = (size_t)510 * 32 * (128 + 2) * 4;   // 8,486,400 bytes
+
+// Address of this GPU's copy of the static decode scratch (kDecodeScratchBytes, for
+// fa_decode_noalloc): the GPU of `stream` (the current one for the null stream); looked up
+// once per GPU with that GPU current, then cached.
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 // bf16 q [B, Hq, Nq, d], k, v [B, Hkv, Nk, d] -> o [B, Hq, Nq, d] bf16, lse [B, Hq, Nq] or null;
 // ws: decode_plan(...).ws_bytes of workspace. d in {64, 128}.
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, void* ws, int B,

@@ -57,7 +57,8 @@ typedef enum {
     FA_ERR_DTYPE = -5,     /* dtype is not one of fa_dtype */
     FA_ERR_SCALE = -6,     /* scale is not finite and > 0 */
     FA_ERR_LAUNCH = -7,    /* the HIP runtime reported an error at launch */
-    FA_ERR_ARG = -8        /* any other invalid argument (e.g. causal not 0/1) */
+    FA_ERR_ARG = -8,       /* any other invalid argument (e.g. causal not 0/1) */
+    FA_ERR_SCRATCH = -9    /* fa_decode_noalloc: the problem needs more than its static scratch */
 } fa_status;
 
 typedef enum {
@@ -218,6 +219,25 @@ size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_noalloc - fa_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernels and results as fa_decode (bit for bit); it calls
+ * no hipMalloc, hipFree or other allocating routine.
+ *
+ * The split states live in a static device array of the library (8,486,400 bytes, one copy
+ * per GPU, held until the process ends): the largest workspace fa_decode_workspace_size gives
+ * for any shape, so no shape is refused today; a shape that needed more would return
+ * FA_ERR_SCRATCH before any launch. The first call on a GPU looks up that GPU's copy (the GPU
+ * of `stream`, the current one for the null stream). Every call on one GPU shares its copy:
+ * calls that overlap in time on one GPU (several streams, several host threads) race and give
+ * undefined outputs; calls on one stream are ordered and safe. No contents need clearing
+ * between calls (every state is written before it is read).
+ */
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int dtype, void* stream);
 
 /* fa_status_string - static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_prep_fp8", "fa_fwd_fp8", "fa_bwd", "fa_fwd_ext",
-                                           "fa_decode_workspace_size", "fa_decode", "fa_status_string", "fa_version"])
+                                           "fa_decode_workspace_size", "fa_decode", "fa_decode_noalloc",
+                                           "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_version_and_status_strings(L):
     from exact_attention_06_amd import _lib
 
-    assert L.fa_version() == 400
+    assert L.fa_version() == 500
     for code, name in _lib.STATUS_NAMES.items():
         s = _lib.status_string(code)
         assert s and s != "unknown status", name
@@ -238,3 +239,27 @@ def test_fwd_ext_argument_errors(L):
         assert ext(L, p) == -2, i
     assert ext(L, [None] * 5, N=0) == 0                      # empty: nothing launched
     assert ext(L, [None] * 5, cu=P, max_seqlen=0) == 0       # packed, every sequence empty
+
+
+def test_decode_noalloc_argument_errors(L):
+    """The allocation-free decoding entry point checks its arguments like fa_decode, before it
+    looks up its scratch or launches anything (nothing here reaches the GPU)."""
+    def dn(ptrs=None, B=2, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128, scale=0.088, causal=0, dtype=1):
+        p = [P] * 5 if ptrs is None else ptrs
+        return L.fa_decode_noalloc(*p, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
+
+    assert dn(d=256) == -4
+    assert dn(dtype=0) == -5
+    assert dn(scale=0.0) == -6
+    assert dn(causal=3) == -8
+    assert dn(Hkv=3) == -3
+    assert dn(Nq=9, Nk=8) == -3
+    for i in range(4):                    # q k v o
+        p = [P] * 5
+        p[i] = None
+        assert dn(p) == -1, i
+        p[i] = P + 4
+        assert dn(p) == -2, i
+    assert dn([None] * 5, Nq=0) == 0      # empty: nothing touched, nothing launched
+    # every shape's workspace fits the static scratch (8,486,400 bytes, the largest any shape needs)
+    assert L.fa_decode_workspace_size(255, 1, 1, 32, 512, 128) == 8486400
