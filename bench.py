@@ -38,7 +38,8 @@ rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
 of the backward kernels) and prints its own JSON line; ``--only-decode`` does the
 same for split-key decoding on the grouped-head 8K-cache workload, ``--only fp8``
 for the FP8 forward (inputs quantised once, untimed) and ``--only NAME`` for the
-bf16 or fp32 forward on the named workload (e.g. short_b64h16n512_d128).
+bf16 or fp32 forward on the named workload (e.g. short_b64h16n512_d128; with
+``--causal`` its causal variant).
 """
 
 from __future__ import annotations
@@ -74,6 +75,7 @@ def parse_args():
     p.add_argument("--only-bwd", action="store_true")
     p.add_argument("--only-decode", action="store_true")
     p.add_argument("--only", default=None, help="fp8, or a forward workload name")
+    p.add_argument("--causal", action="store_true", help="--only: the causal variant of a workload that has one")
     p.add_argument("--only-ext", default=None, help="one grouped-head / window / packed workload")
     p.add_argument("--source-hashes", action="store_true", help="print the kernel families' source hashes")
     p.add_argument("--summarize", default=None, metavar="DIR",
@@ -475,6 +477,11 @@ def main():
             return 2
         wx = WORKLOADS[args.only]
         causal = wx.causal[0]
+        if args.causal:
+            if True not in wx.causal:
+                print(f"--causal: {args.only} has no causal variant", file=sys.stderr)
+                return 2
+            causal = True
         q, k, v = (x.cuda() for x in make_qkv(wx.B, wx.H, wx.N, wx.d, wx.seed, wx.dtype))
         o = torch.empty_like(q)
         lse = torch.empty((wx.B, wx.H, wx.N), dtype=torch.float32, device="cuda")
