@@ -267,8 +267,11 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         qbk = __builtin_amdgcn_readfirstlane(qbk);
         qi = CAUSAL ? numQB - 1 - qbk : qbk;
     } else {
-        // causal: each XCD's range ordered by query block first (costliest blocks first)
-        work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL, bh, qi);
+        // causal, d <= 128: each XCD's range ordered by query block first (costliest blocks
+        // of all its heads first, for the tail). d = 256 (one workgroup per CU, twice the
+        // K/V bytes per key): head by head, costliest block first, so that an XCD's L2 holds
+        // about one head's K and V at a time; the measured order is faster at each size
+        work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL && D <= 128, bh, qi);
     }
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
