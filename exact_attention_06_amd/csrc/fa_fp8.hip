@@ -167,15 +167,15 @@ hipError_t launch_prep(const float* x, void* x8, float* s, const float* signs, i
     return hipGetLastError();
 }
 
-template <int D, int BC, int NQ, int MINB, bool PIPE>
+template <int D, int BC, int NQ, int MINB, bool PIPE, int WAVES = 4, int DSPLIT = 1>
 hipError_t dispatch_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                         const float* sv, void* o, float* lse, int BH, int N, float scale, bool causal,
                         hipStream_t stream) {
     constexpr InKind K = InKind::FP8;
-    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale,
-                                                                         stream)
-                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale,
-                                                                          stream);
+    return causal ? launch_fwd_kernel<K, D, BC, NQ, true, 8, MINB, PIPE, WAVES, false, DSPLIT>(
+                        q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream)
+                  : launch_fwd_kernel<K, D, BC, NQ, false, 8, MINB, PIPE, WAVES, false, DSPLIT>(
+                        q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream);
 }
 
 }  // namespace
@@ -193,12 +193,15 @@ hipError_t launch_prep_fp8(const float* x, void* x8, float* s, const float* sign
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* sq, const float* sk,
                           const float* sv, void* o, float* lse, int BH, int N, int d, float scale, bool causal,
                           hipStream_t stream) {
-    // key blocks of 64 keys (one scale block) or, for d = 128, 32 (half of one; fewer live
-    // registers, as for bf16); conditional rescale threshold 2^8
+    // key blocks of 64 keys (one scale block) or, for d = 128 and 256, 32 (half of one; fewer
+    // live registers, as for bf16); conditional rescale threshold 2^8. d = 256: 8 waves in pairs
+    // that split the head dimension (each wave holds Q and O for 128 columns, the d = 128
+    // footprint), one workgroup of 128 queries per CU, as for bf16
     switch (d) {
         case 64: return dispatch_fp8<64, 64, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         case 128: return dispatch_fp8<128, 32, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
-        case 256: return dispatch_fp8<256, 64, 1, 1, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        case 256:
+            return dispatch_fp8<256, 32, 1, 1, true, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     using PT = typename std::conditional<C::F8, f16x8, bf16x8>::type;
     using PE = typename std::conditional<C::F8, _Float16, bf16_t>::type;
     constexpr float tau = (float)TAU;
-    static_assert(DSPLIT == 1 || (DSPLIT == 2 && !C::F8 && PIPE && WAVES % 2 == 0), "d split: bf16, pipelined, wave pairs");
+    static_assert(DSPLIT == 1 || (DSPLIT == 2 && PIPE && WAVES % 2 == 0), "d split: pipelined, wave pairs");
     constexpr int BR = WAVES / DSPLIT * 32 * NQ;   // queries per workgroup
     constexpr int KST = C::KSTEPS / DSPLIT;        // QK steps of one wave
     constexpr int DTW = C::DT / DSPLIT;            // 32-wide d tiles of O^T of one wave
@@ -436,8 +436,11 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     // K operand of QK step s, 32-key tile t: row 32t + swap_bits23(col), chunk c(s, h)
     constexpr int KREADS = C::F8 ? 2 : 1;              // 16-byte reads per operand
     constexpr int KSPAN = C::F8 ? 4 : 8;               // steps per 16 chunks
-    constexpr int KA = C::KSTEPS < KSPAN ? C::KSTEPS : KSPAN;
-    static_assert(DSPLIT == 1 || (KST % KSPAN == 0 && DTW % 4 == 0), "d split: whole 16-chunk spans per wave");
+    constexpr int KA = KST < KSPAN ? KST : KSPAN;
+    // d split: a wave's steps are whole spans (bf16 d = 256) or a part of one span (e4m3
+    // d = 256: two of its four steps)
+    static_assert(DSPLIT == 1 || ((KST % KSPAN == 0 || KSPAN % KST == 0) && DTW % 4 == 0),
+                  "d split: whole 16-chunk spans, or whole parts of one, per wave");
     const int khd = 256 * (hd * KST / KSPAN);   // the wave's first K chunk span
     const int vhd = 256 * (hd * DTW / 4);       // and first V^T chunk span
     int kaddr[KA][KREADS];
@@ -447,7 +450,8 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         for (int s = 0; s < KA; ++s)
 #pragma unroll
             for (int u = 0; u < KREADS; ++u) {
-                const int c = C::F8 ? 4 * s + 2 * h + u : 2 * s + h;
+                const int w = (hd * KST + s) % KSPAN;   // the step's place in its span
+                const int c = C::F8 ? 4 * w + 2 * h + u : 2 * w + h;
                 kaddr[s][u] = rr * C::ROW_BYTES + 16 * k_slot<C::KSWZ>(rr, c);
             }
     }
@@ -805,7 +809,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
             const float l_tot = pair_sum(l_run[n]);   // lanes l and l^32 hold the two halves of a row's sum
             const float inv = l_tot > 0.f ? svmax / l_tot : 0.f;
             if (qrow[n] < N) {
-                float* const orow = O + head_off + (size_t)qrow[n] * D + 4 * h;
+                float* const orow = O + head_off + (size_t)qrow[n] * D + hd * (D / DSPLIT) + 4 * h;
 #pragma unroll
                 for (int e = 0; e < DTW; ++e)
 #pragma unroll
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
                         *(f32x4*)(orow + 32 * e + 8 * a) =
                             f32x4{acc[n][e][4 * a] * inv, acc[n][e][4 * a + 1] * inv, acc[n][e][4 * a + 2] * inv,
                                   acc[n][e][4 * a + 3] * inv};
-                if (LSE != nullptr && h == 0)
+                if (LSE != nullptr && h == 0 && hd == 0)
                     LSE[qbase + qrow[n]] = l_tot > 0.f ? (m_run[n] + __log2f(l_tot)) * kLn2 : -INFINITY;
             }
         }
