@@ -81,6 +81,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, i
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
+__device__ __forceinline__ i32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
 
 // XCD-aware work index: the dispatcher hands consecutive workgroup ids to the 8 XCDs in
 // turn; remap so that each XCD walks a contiguous range of work items (a contiguous range

@@ -77,7 +77,7 @@ struct FwdCfg {
     static constexpr int K_BYTES = BC * ROW_BYTES;
     static constexpr int V_BYTES = BC * VROW_BYTES;
     static constexpr int K_LOADS = K_BYTES / 16 / NT;            // direct loads per thread
-    static constexpr int V_LOADS = F8 ? BC * D / 16 / NT : V_BYTES / 16 / NT;
+    static constexpr int V_LOADS = F8 ? BC * D / 8 / NT : V_BYTES / 16 / NT;   // FP8: 8-byte loads
     static_assert(K_LOADS >= 1 && K_LOADS * NT * 16 == K_BYTES, "K tile must split evenly");
     static_assert(V_LOADS >= 1, "V tile must split evenly");
     // FP8: a key block lies inside one 64-row scale block of K and V
@@ -381,16 +381,17 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     constexpr int VRPL = 1024 / C::VROW_BYTES;
     int voff0;
     if constexpr (C::F8) {
-        // register-staged: load i of a thread reads e4m3 chunk x = tid + 256 i (16 values),
-        // row x / (D/16); 256 is a multiple of D/16, so rows of successive loads are
-        // 256 / (D/16) apart
-        voff0 = (tid / (D / 16)) * C::ROW_BYTES + 16 * (tid % (D / 16));
+        // register-staged: load i of a thread reads the 8 e4m3 values x = tid + NT i of the
+        // tile (row x / (D/8), fp16 chunk x % (D/8) once expanded); NT is a multiple of D/8, so
+        // rows of successive loads are NT / (D/8) apart. 16 consecutive lanes then write 16
+        // consecutive fp16 chunks of one row (or two 128-byte rows), all 64 banks once.
+        voff0 = (tid / (D / 8)) * C::ROW_BYTES + 8 * (tid % (D / 8));
     } else {
         const int r = VRPL * wave + lane / C::VCPR;
         voff0 = r * C::ROW_BYTES + 16 * v_slot<C::VSWZ>(r, lane % C::VCPR);
     }
     auto voff_of = [&](int i) {
-        if constexpr (C::F8) return voff0 + (NT / (D / 16)) * C::ROW_BYTES * i;
+        if constexpr (C::F8) return voff0 + (NT / (D / 8)) * C::ROW_BYTES * i;
         return voff0 + WAVES * VRPL * C::ROW_BYTES * i;   // rows WAVES VRPL apart keep the V swizzle
     };
     auto load_k = [&](int kb, uint8_t* dst) {
@@ -398,12 +399,12 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         for (int i = 0; i < C::K_LOADS; ++i)
             lds_dma16(rK, dst + 1024 * (wave + WAVES * i), koff_of(i) + kb * C::ROW_BYTES);
     };
-    i32x4 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
+    i32x2 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
     auto load_v = [&](int kb, uint8_t* dst) {
 #pragma unroll
         for (int i = 0; i < C::V_LOADS; ++i) {
             if constexpr (C::F8)
-                vst[i] = buffer_load16(rV, voff_of(i) + kb * C::ROW_BYTES);
+                vst[i] = buffer_load8(rV, voff_of(i) + kb * C::ROW_BYTES);
             else
                 lds_dma16(rV, dst + 1024 * (wave + WAVES * i), voff_of(i) + kb * C::ROW_BYTES);
         }
@@ -414,18 +415,15 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
 #pragma unroll
             for (int i = 0; i < C::V_LOADS; ++i) {
                 const int x = tid + NT * i;
-                const int r = x / (D / 16);
-                const int c8 = x % (D / 16);   // 16 e4m3 values = fp16 chunks 2 c8 and 2 c8 + 1
-                i32x4 lo, hi;
+                const int r = x / (D / 8);
+                const int c = x % (D / 8);   // 8 e4m3 values = fp16 chunk c
+                i32x4 w;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int wa = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, false));
-                    const int wb = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, true));
-                    if (u < 2) { lo[2 * u] = wa; lo[2 * u + 1] = wb; }
-                    else { hi[2 * (u - 2)] = wa; hi[2 * (u - 2) + 1] = wb; }
+                for (int u = 0; u < 2; ++u) {
+                    w[2 * u] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, false));
+                    w[2 * u + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vst[i][u], 1.f, true));
                 }
-                *(i32x4*)(dst + r * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(r, 2 * c8)) = lo;
-                *(i32x4*)(dst + r * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(r, 2 * c8 + 1)) = hi;
+                *(i32x4*)(dst + r * C::VROW_BYTES + 16 * v_slot<C::VSWZ>(r, c)) = w;
             }
         }
     };
