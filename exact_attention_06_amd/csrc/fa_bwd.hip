@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void bwd_dq_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
     int bh, qi;   // causal: heaviest blocks first, across the XCD's heads
-    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL, bh, qi);
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL ? 0 : 1, bh, qi);
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
     const int q0w = q0 + 32 * wave;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
     int bh, kbi;   // causal: low key blocks see the most queries and come first (across the XCD's heads)
-    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL, bh, kbi);
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL ? 0 : 1, bh, kbi);
     const int k0 = kbi * BK;
     const int k0w = k0 + 32 * wave;
     const int krow = k0w + col;
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(
     const bool pwave = wave < 4;
     const int h = lane >> 5, col = lane & 31;
     int bh, kbi;   // causal: low key blocks see the most queries and come first (across the XCD's heads)
-    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL, bh, kbi);
+    work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numKB, CAUSAL ? 0 : 1, bh, kbi);
     const int k0 = kbi * BK;
     const int k0w = k0 + 32 * pair;
     const int krow = k0w + col;

@@ -93,21 +93,26 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
     return (id & 7) * (total >> 3) + (id >> 3);
 }
 
-// Work item w (after xcd_remap) of total = rows x nblk items, as (row, block index). Plain:
-// row-major (one row's blocks together). Block-major: each XCD's contiguous range of rows is
-// walked by block index first, so that for causal problems the costliest blocks of all of the
-// XCD's rows are dispatched before any lighter one (longest first), with the same rows per XCD.
-__device__ __forceinline__ void work_item(int w, int total, int nblk, bool block_major, int& row, int& blk) {
+// Work item w (after xcd_remap) of total = rows x nblk items, as (row, block index).
+// group == 1: row-major (one row's blocks together). Otherwise each XCD's contiguous range of
+// rows is walked in groups of `group` rows (all of the range if group <= 0 or if it does not
+// divide the range), each group by block index first: for causal problems the costliest
+// blocks of the group's rows are dispatched before any lighter one (longest first), and only
+// the group's rows share the XCD's L2 at a time.
+__device__ __forceinline__ void work_item(int w, int total, int nblk, int group, int& row, int& blk) {
     row = w / nblk;
     blk = w - row * nblk;
-    if (block_major && (total & 7) == 0) {
+    if (group != 1 && (total & 7) == 0) {
         const int per = total >> 3;
         const int nh = per / nblk;
         if (nh * nblk == per) {
+            const int G = (group > 0 && group < nh && nh % group == 0) ? group : nh;
             const int xcd = w / per;
             const int k = w - xcd * per;
-            blk = k / nh;
-            row = xcd * nh + (k - blk * nh);
+            const int g = k / (G * nblk);
+            const int kk = k - g * G * nblk;
+            blk = kk / G;
+            row = xcd * nh + g * G + (kk - blk * G);
         }
     }
 }

@@ -194,12 +194,14 @@ hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8, const 
                           const float* sv, void* o, float* lse, int BH, int N, int d, float scale, bool causal,
                           hipStream_t stream) {
     // key blocks of 64 keys (one scale block) or, for d = 128 and 256, 32 (half of one; fewer
-    // live registers, as for bf16); conditional rescale threshold 2^8. d = 256: 8 waves in pairs
-    // that split the head dimension (each wave holds Q and O for 128 columns, the d = 128
-    // footprint), one workgroup of 128 queries per CU, as for bf16
+    // live registers, as for bf16); conditional rescale threshold 2^8. d = 128: 8 waves (256
+    // queries) share each K/V tile, one workgroup per CU; the 4 KB e4m3 K tile is loaded by
+    // four of them, and all eight expand V (+1.4% over 4-wave workgroups). d = 256: 8 waves in
+    // pairs that split the head dimension (each wave holds Q and O for 128 columns, the
+    // d = 128 footprint), one workgroup of 128 queries per CU, as for bf16
     switch (d) {
         case 64: return dispatch_fp8<64, 64, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
-        case 128: return dispatch_fp8<128, 32, 1, 2, true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
+        case 128: return dispatch_fp8<128, 32, 1, 1, true, 8>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         case 256:
             return dispatch_fp8<256, 32, 1, 1, true, 8, 2>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, causal, stream);
         default: return hipErrorInvalidValue;

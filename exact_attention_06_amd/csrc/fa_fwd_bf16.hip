@@ -4,7 +4,7 @@
 // Tile choices per head dimension (keys per block BC, 32-query tiles per wave NQ,
 // workgroups per CU MINB, score pipeline PIPE):
 //   d =  64: BC 64, NQ 1, 2 workgroups per CU, pipelined
-//   d = 128: BC 32, NQ 1, pipelined; 8 waves per workgroup (one per CU) for non-causal
+//   d = 128: BC 32, NQ 1, pipelined; 8 waves per workgroup (one per CU) for
 //            N >= 2048, else 4 waves and 2 workgroups per CU (BC 64 needs more registers than
 //            two workgroups per CU leave, and the spill reloads stall on the tile loads in
 //            flight, since vector-memory counters retire in order). (NQ 2 halves the LDS operand
@@ -75,10 +75,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     switch (d) {
         case 64: return dispatch<64, 64, 1, 2, true>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 128:
-            // long non-causal rows: 8 waves (256 queries) per workgroup share each K/V tile,
-            // which halves the tile traffic per FLOP (+3% at N = 8k); otherwise 4 waves, whose
-            // smaller workgroups balance causal and short problems better
-            if (!causal && N >= 2048)
+            // rows of 2048 or more: 8 waves (256 queries) per workgroup share each K/V tile,
+            // which halves the tile traffic per FLOP (+3% at N = 8k non-causal, +1-4% causal);
+            // shorter rows keep 4 waves, whose smaller workgroups balance better
+            if (N >= 2048)
                 return dispatch<128, 32, 1, 1, true, 8>(q, k, v, o, lse, BH, N, scale, causal, stream);
             return dispatch<128, 32, 1, 2, true, 4>(q, k, v, o, lse, BH, N, scale, causal, stream);
         case 256:

@@ -50,6 +50,7 @@
 //   an output by more than the 6e-2 budget. For the same reason O is written in fp32.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -76,9 +77,12 @@ struct FwdCfg {
     static constexpr int CH = BC / 16;                      // 16-key chunks of the PV product
     static constexpr int K_BYTES = BC * ROW_BYTES;
     static constexpr int V_BYTES = BC * VROW_BYTES;
-    static constexpr int K_LOADS = K_BYTES / 16 / NT;            // direct loads per thread
+    // direct loads per thread; a K tile smaller than one 1 KB region per wave is loaded by its
+    // first K_BYTES / 1024 waves, one region each
+    static constexpr bool K_PART = K_BYTES < 16 * NT;
+    static constexpr int K_LOADS = K_PART ? 1 : K_BYTES / 16 / NT;
     static constexpr int V_LOADS = F8 ? BC * D / 8 / NT : V_BYTES / 16 / NT;   // FP8: 8-byte loads
-    static_assert(K_LOADS >= 1 && K_LOADS * NT * 16 == K_BYTES, "K tile must split evenly");
+    static_assert(K_PART ? K_BYTES % 1024 == 0 : K_LOADS * NT * 16 == K_BYTES, "K tile must split evenly");
     static_assert(V_LOADS >= 1, "V tile must split evenly");
     // FP8: a key block lies inside one 64-row scale block of K and V
     static_assert(!F8 || 64 % BC == 0, "FP8 key blocks must divide the 64-row scale blocks");
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
     void* __restrict__ Ov, float* __restrict__ LSE, int N, int numQB, int nsb, float c2 /* scale*log2(e) */,
-    FwdExt ext) {
+    int hgroup, FwdExt ext) {
     static_assert(!(EXT && KIND == InKind::FP8), "extended problems take bf16 inputs");
     constexpr int NT = 64 * WAVES;    // threads per workgroup
     using C = FwdCfg<KIND, D, BC, NT>;
@@ -267,11 +271,9 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         qbk = __builtin_amdgcn_readfirstlane(qbk);
         qi = CAUSAL ? numQB - 1 - qbk : qbk;
     } else {
-        // causal, d <= 128: each XCD's range ordered by query block first (costliest blocks
-        // of all its heads first, for the tail). d = 256 (one workgroup per CU, twice the
-        // K/V bytes per key): head by head, costliest block first, so that an XCD's L2 holds
-        // about one head's K and V at a time; the measured order is faster at each size
-        work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL && D <= 128, bh, qi);
+        // causal: each XCD's heads in groups of hgroup (launch_fwd_kernel), each group ordered
+        // by query block first (costliest blocks first)
+        work_item(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, numQB, CAUSAL ? hgroup : 1, bh, qi);
     }
     const int qb = CAUSAL ? (numQB - 1 - qi) : qi;
     const int q0 = qb * BR;
@@ -395,9 +397,13 @@ __global__ __launch_bounds__(64 * WAVES, MINB) void fwd_kernel(
         return voff0 + WAVES * VRPL * C::ROW_BYTES * i;   // rows WAVES VRPL apart keep the V swizzle
     };
     auto load_k = [&](int kb, uint8_t* dst) {
+        if constexpr (C::K_PART) {
+            if (wave < C::K_BYTES / 1024) lds_dma16(rK, dst + 1024 * wave, koff_of(0) + kb * C::ROW_BYTES);
+        } else {
 #pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i)
-            lds_dma16(rK, dst + 1024 * (wave + WAVES * i), koff_of(i) + kb * C::ROW_BYTES);
+            for (int i = 0; i < C::K_LOADS; ++i)
+                lds_dma16(rK, dst + 1024 * (wave + WAVES * i), koff_of(i) + kb * C::ROW_BYTES);
+        }
     };
     i32x2 vst[C::F8 ? C::V_LOADS : 1];   // FP8 V staging
     auto load_v = [&](int kb, uint8_t* dst) {
@@ -895,8 +901,25 @@ hipError_t launch_fwd_kernel(const void* q, const void* k, const void* v, const 
     if (EXT && ext.cu != nullptr)
         total = std::min(total, (long long)ext.Hq * (((long long)ext.ntot + (long long)ext.nseq * (BR - 1)) / BR));
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+    // causal: heads walked block-first per XCD, all of the XCD's heads at once or, with 16 or
+    // more heads per XCD, in groups of about two rounds of its workgroup slots (32 CUs x MINB):
+    // fewer heads' K and V then share its L2, and each group still dispatches its costliest
+    // blocks first (at least two heads per group: one alone leaves its light blocks for the
+    // group's end). With 8 or fewer heads per XCD the groups measured no better. d = 256 (one
+    // workgroup per CU, twice the K/V bytes per key): head by head
+    int hgroup = 1;
+    if (CAUSAL && D <= 128) {
+        hgroup = 0;   // the XCD's whole range
+        if (BH % 8 == 0 && BH / 8 >= 16) {
+            const int nh = BH / 8;   // heads per XCD
+            int g = std::min(nh, std::max(2, 2 * 32 * MINB / std::max(1, numQB)));
+            while (nh % g != 0) --g;
+            hgroup = g;
+        }
+    }
     hipLaunchKernelGGL((fwd_kernel<KIND, D, BC, NQ, CAUSAL, TAU, MINB, PIPE, WAVES, EXT, DSPLIT>), dim3((unsigned)total),
-                       dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, o, lse, N, numQB, nsb, scale * kLog2e, ext);
+                       dim3(64 * WAVES), 0, stream, q, k, v, sq, sk, sv, o, lse, N, numQB, nsb, scale * kLog2e, hgroup,
+                       ext);
     return hipGetLastError();
 }
 
