@@ -70,6 +70,8 @@ CASES = [  # (B, Hq, Hkv, N, d, causal, window, lengths or None)
     (1, 2, 1, sum(_M65), 128, True, (-1, -1), _M65),
     (1, 2, 1, sum(_M90), 128, False, (-1, -1), _M90),
     (1, 4, 2, sum(_M90), 64, True, (40, 0), _M90),
+    # 16 heads per XCD: the causal grid walks them in groups of 8 (4-wave workgroups)
+    (8, 16, 4, 2048, 128, True, (-1, -1), None),
 ]
 
 

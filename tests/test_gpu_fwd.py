@@ -88,6 +88,23 @@ def test_bf16_large_grid_full_compare(shape):
     t.check()
 
 
+# causal grids with 16 or more heads per XCD walk the heads in groups, each group query block
+# first (launch_fwd_kernel picks the group size): 8-wave d = 128 with a ragged last block (4 of
+# the XCD's 16 heads per group), 4-wave d = 128 below 2048 (16 of 32) and d = 64 (4 of 16)
+HEAD_GROUP_GRIDS = [(8, 16, 2100, 128), (16, 16, 1024, 128), (8, 16, 4096, 64)]
+
+
+@pytest.mark.parametrize("shape", HEAD_GROUP_GRIDS)
+def test_causal_head_groups_whole_output(shape):
+    B, H, N, d = shape
+    say(f"bf16 causal head groups {shape}")
+    q, k, v = make_qkv(B, H, N, d, seed=650 + N + d, dtype="bf16")
+    o, lse = run_gpu(q, k, v, True)
+    t = compare_heads(o, lse, lambda b, h: attention_head_fp64(q[b, h], k[b, h], v[b, h], d ** -0.5, True),
+                      [(b, h) for b in range(B) for h in range(H)], f"causal head groups {shape}")
+    t.check()
+
+
 # N <= 128 at d = 64 and 128 runs the short-sequence kernel (a whole head in one workgroup's
 # LDS, exact two-pass softmax): lengths from one key to the full 128, with ragged last blocks
 SHORT = [(2, 3, 1, 64), (1, 2, 17, 128), (2, 2, 32, 64), (1, 3, 33, 128), (1, 2, 64, 128), (2, 1, 100, 64),
