@@ -29,7 +29,7 @@
 //
 // The FP8 forward itself is the shared fused kernel (fa_fwd_kernel.h) instantiated for e4m3
 // Q, K, V: e4m3 QK^T on the matrix cores with the block scales folded into the softmax FMA,
-// V expanded exactly to bf16 in LDS with its block scale carried by P, bf16 P.
+// V expanded exactly to fp16 in LDS with its block scale carried by P, fp16 P and an fp32 O.
 #include <cmath>
 
 #include "fa_common.h"

@@ -15,11 +15,13 @@
 //   partner lane l^32: row max and row sum are in-register reductions plus one
 //   v_permlane32_swap. A wave's queries never interact with another wave's (split-Q).
 // - K rows are fed to the MFMA in the order swap_bits23, so the S^T result registers are
-//   already the B operand (P^T) of O^T += V_j^T P^T in bf16; P never leaves registers.
-// - V^T is read from the row-major bf16 V tile with ds_read_b64_tr_b16 (8 keys of one d
+//   already the B operand (P^T) of O^T += V_j^T P^T in bf16 (FP8: fp16); P never leaves
+//   registers.
+// - V^T is read from the row-major 16-bit V tile with ds_read_b64_tr_b16 (8 keys of one d
 //   column per lane in two reads).
-// - K/V blocks go from HBM straight into LDS (buffer_load ... lds, no staging registers);
-//   rows past N read as zero through the buffer's range check. Tiles are unpadded and
+// - K/V blocks go from HBM straight into LDS (buffer_load ... lds, no staging registers;
+//   FP8 V passes through registers to be expanded); rows past N read as zero through the
+//   buffer's range check. Tiles are unpadded and
 //   XOR-swizzled in 16-byte chunks so that the MFMA operand reads and the transposing V
 //   reads are free of bank conflicts.
 // - Two-stage software pipeline: while the softmax of block j runs on the vector ALUs, the

@@ -99,7 +99,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *          x8 = e4m3(x_rotated / s), the division done in fp32.
  *   signs  [d] fp32 of +1/-1 (input), the diagonal D; NULL skips the rotation
  *          (plain block quantisation, e.g. for V).
- * The rotation is computed in fp32 with a fast Walsh-Hadamard transform.
+ * The rotation is computed in fp64 with a fast Walsh-Hadamard transform and
+ * rounded once to fp32 (the float64 product x M of the definition, rounded).
  */
 int fa_prep_fp8(const float* x, void* x8, float* s, const float* signs,
                 int B, int H, int N, int d, void* stream);
