@@ -62,8 +62,14 @@ __device__ __forceinline__ double quad_xor_d(double x) {
     return __hiloint2double(hi, lo);
 }
 
+// workgroups per CU the register budget is held to: the kernel streams memory, and the loads
+// of more resident workgroups hide more latency (d = 128: 5, where the compiler would otherwise
+// take 108 registers and leave room for 4)
 template <int D>
-__global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
+constexpr int kPrepMinBlocks = D <= 64 ? 8 : D <= 128 ? 5 : 2;
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads, kPrepMinBlocks<D>) void prep_fp8_kernel(const float* __restrict__ X, uint8_t* __restrict__ X8,
                                                             float* __restrict__ S, const float* __restrict__ signs,
                                                             int N, int nsb, double inv_sqrt_d) {
     constexpr int NV = D / 4;   // values per thread: x[4 k + j] is element 16 k + 4 qd + j
@@ -106,13 +112,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_fp8_kernel(const float* __r
                     y[i + st] = a - b;
                 }
         // cross-thread butterflies: element bits 2 and 3 (lane xor 1, xor 2); the lower
-        // partner keeps x + y, the upper one y - x, i.e. (+-x) + y
+        // partner keeps x + y, the upper one y - x, i.e. (+-x) + y, one fused multiply-add
+        // (the product by +-1 is exact, so it rounds as the sum alone)
         const double sg1 = (qd & 1) ? -1.0 : 1.0;
         const double sg2 = (qd & 2) ? -1.0 : 1.0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) y[i] = __dadd_rn(quad_xor_d<0xB1>(y[i]), __dmul_rn(y[i], sg1));
+        for (int i = 0; i < NV; ++i) y[i] = __fma_rn(y[i], sg1, quad_xor_d<0xB1>(y[i]));
 #pragma unroll
-        for (int i = 0; i < NV; ++i) y[i] = __dadd_rn(quad_xor_d<0x4E>(y[i]), __dmul_rn(y[i], sg2));
+        for (int i = 0; i < NV; ++i) y[i] = __fma_rn(y[i], sg2, quad_xor_d<0x4E>(y[i]));
         // signs and 1/sqrt(d) in one multiply (+-c is exact), then the one rounding to fp32
 #pragma unroll
         for (int i = 0; i < NV; i += 4) {
