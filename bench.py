@@ -37,7 +37,8 @@ rocprofv3 byte counters); ``--only-headline`` skips the extra workloads;
 ``--only-bwd`` times only the backward on the headline shape (for kernel traces
 of the backward kernels) and prints its own JSON line; ``--only-decode`` does the
 same for split-key decoding on the grouped-head 8K-cache workload, ``--only fp8``
-for the FP8 forward (inputs quantised once, untimed) and ``--only NAME`` for the
+for the FP8 forward (inputs quantised once, untimed), ``--only fp8-prep`` for the
+rotation and quantisation of one tensor of that workload, and ``--only NAME`` for the
 bf16 or fp32 forward on the named workload (e.g. short_b64h16n512_d128; with
 ``--causal`` its causal variant).
 """
@@ -74,7 +75,7 @@ def parse_args():
     p.add_argument("--calib-copy", action="store_true")
     p.add_argument("--only-bwd", action="store_true")
     p.add_argument("--only-decode", action="store_true")
-    p.add_argument("--only", default=None, help="fp8, or a forward workload name")
+    p.add_argument("--only", default=None, help="fp8, fp8-prep, or a forward workload name")
     p.add_argument("--causal", action="store_true", help="--only: the causal variant of a workload that has one")
     p.add_argument("--only-ext", default=None, help="one grouped-head / window / packed workload")
     p.add_argument("--source-hashes", action="store_true", help="print the kernel families' source hashes")
@@ -457,6 +458,18 @@ def main():
                                                  f"Nk={wd.Nk} d={wd.d} bf16"}}))
         return 0
 
+    if args.only == "fp8-prep":
+        # the rotation + quantisation of one tensor of the FP8 workload (Q: rotated)
+        wf = WORKLOADS["fp8_b4h16n8k_d128"]
+        q, _, _, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))
+        q8, sq = fa_prep_fp8(q, signs)
+        m = time_launches(torch, lambda: fa_prep_fp8(q, signs, q8, sq), args.steps, args.warmup, 100.0)
+        nbytes = q.numel() * 5 + sq.numel() * 4
+        print(json.dumps({"metric": "FP8 rotation + quantisation GB/s (4 B read + 1 B written per element)",
+                          "value": round(nbytes / m / 1e6, 1), "unit": "GB/s", "ms_per_step": round(m, 4),
+                          "steps": args.steps,
+                          "config": {"workload": f"fa_prep_fp8 B={wf.B} H={wf.H} N={wf.N} d={wf.d} rotated"}}))
+        return 0
     if args.only == "fp8":
         wf = WORKLOADS["fp8_b4h16n8k_d128"]
         q, k, v, signs = (x.cuda() for x in make_fp8_inputs(wf.B, wf.H, wf.N, wf.d, wf.seed))
