@@ -98,7 +98,7 @@ def check_vs_deq(o, lse, o_deq, lse_deq, label, o_true=None):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 300, 128), (2, 2, 128, 64), (1, 1, 200, 256), (1, 1, 1, 128),
-                                   (1, 2, 2100, 128), (2, 2, 700, 256), (1, 1, 33, 256)])
+                                   (1, 2, 2100, 128), (2, 2, 700, 256), (1, 1, 33, 256), (2, 4, 4000, 128)])
 def test_fwd_fp8_small(shape, causal):
     say(f"fwd fp8 {shape} causal={causal}")
     B, H, N, d = shape

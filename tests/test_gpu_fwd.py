@@ -90,8 +90,11 @@ def test_bf16_large_grid_full_compare(shape):
 
 # causal grids with 16 or more heads per XCD walk the heads in groups, each group query block
 # first (launch_fwd_kernel picks the group size): 8-wave d = 128 with a ragged last block (4 of
-# the XCD's 16 heads per group), 4-wave d = 128 below 2048 (16 of 32) and d = 64 (4 of 16)
-HEAD_GROUP_GRIDS = [(8, 16, 2100, 128), (16, 16, 1024, 128), (8, 16, 4096, 64)]
+# the XCD's 16 heads per group), 4-wave d = 128 below 2048 (16 of 32) and d = 64 (4 of 16);
+# and a causal d = 256 grid, whose order is head by head
+HEAD_GROUP_GRIDS = [(8, 16, 2100, 128), (16, 16, 1024, 128), (8, 16, 4096, 64),
+                    # d = 256 walks each XCD's heads one after another (costliest block first)
+                    (2, 16, 1100, 256)]
 
 
 @pytest.mark.parametrize("shape", HEAD_GROUP_GRIDS)
